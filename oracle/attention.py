@@ -1,0 +1,188 @@
+"""Plain float64 attention, written straight from the definition (test infrastructure).
+
+Sources (web pages; cited by title and section):
+
+* "Attention 机制详解：从 Self-Attention 到 Multi-Query Attention" (guijiagi.com),
+  §2.1 (the formula softmax(QK^T / sqrt(d_k)) V), §2.2 (masked positions get
+  -inf before the softmax), §5.2 (GQA: each K/V head serves n_heads/n_kv_heads
+  consecutive query heads, via repeat_interleave on the head axis).
+* "拆开 LLM（二）：手撕注意力" (blog.kerro.cn), section "手撕三种打分函数"
+  (softmax with the row maximum subtracted first), section
+  "从对齐机器到 self-attention" (logits -> mask with -inf -> softmax -> weights
+  times V; the causal mask is lower-triangular, True = visible), section
+  "KV cache" (a new token appends its k, v, then attends over every cached
+  position with no mask), section "试一试" (a window that keeps the last W
+  positions, the current one included).
+* "LLM 核心技术：Attention 机制的实现与优化" (zeeklog.com), sections on SWA
+  (each token sees only the previous W tokens) and PagedAttention (the KV cache
+  lives in fixed-size pages of a global pool, reached through a per-sequence
+  page table).
+
+Nothing here is blocked, fused or reordered beyond the definition: for each
+(batch, query head) the full score matrix is formed with one matrix product,
+masked, normalised row by row and multiplied by V. Rows are independent, so a
+row subset (``attention_rows``) or row chunks give the same numbers as the full
+matrix.
+
+Readings taken where the pages leave a point open:
+
+* Window: key j is visible to query position p iff p - W < j <= p (W keys,
+  the query's own position included); ``window == 0`` means no window. Only
+  causal windows appear on the pages, so a window requires ``causal``.
+* Causal alignment when Sq != Sk: bottom-right. Query row i sits at absolute
+  position i + (Sk - Sq); this is the only alignment under which decoding one
+  token against the cache equals the last row of a full causal pass.
+* GQA: query head h reads K/V head h // (Hq // Hkv).
+* Paged cache: ``pool[page, kv_head, slot, d]``; the page table is the ragged
+  concatenation of every sequence's pages in logical order, sequence b owning
+  ceil(seq_lens[b] / page_size) entries; tokens at or beyond seq_lens[b] are
+  never read.
+
+This module is test infrastructure. It is imported by the tests, by the smoke
+check and by the CPU-baseline leg of the benchmark, never by the library.
+"""
+
+import numpy as np
+
+
+def visible(Sq, Sk, causal, window):
+    """Boolean [Sq, Sk] visibility of key j to query row i.
+
+    Causal masking keeps keys at or before the query's position (lower
+    triangle, "拆开 LLM（二）", section "从对齐机器到 self-attention"); a window
+    W additionally drops keys more than W - 1 positions back ("LLM 核心技术",
+    section SWA). Query row i is at position i + Sk - Sq (bottom-right).
+    """
+    pos = np.arange(Sq)[:, None] + (Sk - Sq)
+    j = np.arange(Sk)[None, :]
+    vis = np.ones((Sq, Sk), dtype=bool)
+    if causal:
+        vis &= j <= pos
+    if window > 0:
+        if not causal:
+            raise ValueError("a window is only defined together with causal masking")
+        vis &= j > pos - window
+    return vis
+
+
+def softmax_rows(x):
+    """Row softmax with the row maximum subtracted first.
+
+    "拆开 LLM（二）", section "手撕三种打分函数": shifting a row by a constant
+    does not change its softmax, and after subtracting the maximum the largest
+    exponent is exp(0) = 1, so nothing overflows; -inf entries become exactly 0.
+    """
+    m = np.max(x, axis=-1, keepdims=True)
+    e = np.exp(x - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def _scores(qrows, k, scale, vis_rows):
+    # "Attention 机制详解" §2.2: scores = Q K^T scaled, masked entries -> -inf
+    # before the softmax ("拆开 LLM（二）" pitfalls 1 and 2: -inf, never 0, and
+    # never after the softmax).
+    s = (qrows @ k.T) * scale
+    return np.where(vis_rows, s, -np.inf)
+
+
+def _kv_head(h, Hq, Hkv):
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    # "Attention 机制详解" §5.2: repeat_interleave(n_rep) on the head axis, so
+    # query head h uses K/V head h // n_rep.
+    return h // (Hq // Hkv)
+
+
+def attention_weights(q, k, scale, causal=False, window=0):
+    """Softmax weights P for one head: q [Sq, D], k [Sk, D] -> [Sq, Sk]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    vis = visible(q.shape[0], k.shape[0], causal, window)
+    return softmax_rows(_scores(q, k, scale, vis))
+
+
+def attention_rows(q, k, v, b, h, rows, scale, causal=False, window=0):
+    """Output rows ``rows`` of query head h in batch b, as float64 [len(rows), D].
+
+    q: [B, Hq, Sq, D]; k, v: [B, Hkv, Sk, D]. Same arithmetic as ``attention``
+    restricted to the listed rows (each row of the softmax is independent).
+    """
+    Sq, Sk = q.shape[2], k.shape[2]
+    g = _kv_head(h, q.shape[1], k.shape[1])
+    rows = np.asarray(rows, dtype=np.int64)
+    qr = np.asarray(q[b, h][rows], dtype=np.float64)
+    kb = np.asarray(k[b, g], dtype=np.float64)
+    vb = np.asarray(v[b, g], dtype=np.float64)
+    vis = visible(Sq, Sk, causal, window)[rows]
+    p = softmax_rows(_scores(qr, kb, scale, vis))
+    return p @ vb
+
+
+def attention(q, k, v, scale, causal=False, window=0, row_chunk=2048):
+    """Full attention output, float64 [B, Hq, Sq, D].
+
+    q: [B, Hq, Sq, D]; k, v: [B, Hkv, Sk, D] (any real dtype; converted to
+    float64 exactly). For every (b, h): O = softmax(mask(Q K^T * scale)) V,
+    "Attention 机制详解" §2.1–2.2. ``row_chunk`` only bounds memory.
+    """
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    out = np.empty((B, Hq, Sq, v.shape[3]), dtype=np.float64)
+    vis = visible(Sq, Sk, causal, window)
+    for b in range(B):
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            kb = np.asarray(k[b, g], dtype=np.float64)
+            vb = np.asarray(v[b, g], dtype=np.float64)
+            for r0 in range(0, Sq, row_chunk):
+                r1 = min(Sq, r0 + row_chunk)
+                qr = np.asarray(q[b, h, r0:r1], dtype=np.float64)
+                p = softmax_rows(_scores(qr, kb, scale, vis[r0:r1]))
+                out[b, h, r0:r1] = p @ vb
+    return out
+
+
+def sequence_pages(seq_lens, page_size):
+    """(first, count) of each sequence's entries in the ragged page table.
+
+    Sequence b owns ceil(seq_lens[b] / page_size) consecutive entries, after
+    those of sequences 0 .. b-1 ("Attention From Scratch", 学习路径 §6: a page
+    table records each sequence's pages).
+    """
+    counts = [(int(n) + page_size - 1) // page_size for n in seq_lens]
+    firsts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64) if counts else []
+    return list(zip([int(f) for f in firsts], counts))
+
+
+def gather_sequence(pool, page_table, seq_lens, page_size, b):
+    """Contiguous [Hkv, n, D] float64 K (or V) of sequence b, n = seq_lens[b].
+
+    Logical page p of sequence b is physical page page_table[first_b + p];
+    token t lives at pool[page, :, t % page_size, :] ("LLM 核心技术", section
+    PagedAttention: a page table maps the logical cache onto non-contiguous
+    physical blocks). Pages are concatenated in logical order and cut at n.
+    """
+    first, count = sequence_pages(seq_lens, page_size)[b]
+    n = int(seq_lens[b])
+    phys = np.asarray(page_table[first:first + count], dtype=np.int64)
+    blocks = np.asarray(pool[phys], dtype=np.float64)  # [count, Hkv, ps, D]
+    flat = blocks.transpose(1, 0, 2, 3).reshape(blocks.shape[1], count * page_size, -1)
+    return flat[:, :n, :]
+
+
+def decode_paged(q, k_pool, v_pool, page_table, seq_lens, page_size, scale):
+    """One decode step over a paged cache, float64 [B, Hq, D].
+
+    q: [B, Hq, D] (the new token of each sequence, whose k, v are already in
+    the cache); pools: [num_pages, Hkv, page_size, D]. The new token attends
+    to every cached position 0 .. seq_lens[b]-1 with no mask ("拆开 LLM（二）",
+    section "KV cache").
+    """
+    B, Hq, D = q.shape
+    out = np.empty((B, Hq, v_pool.shape[3]), dtype=np.float64)
+    for b in range(B):
+        kb = gather_sequence(k_pool, page_table, seq_lens, page_size, b)[None]
+        vb = gather_sequence(v_pool, page_table, seq_lens, page_size, b)[None]
+        qb = np.asarray(q[b], dtype=np.float64)[None, :, None, :]
+        out[b] = attention(qb, kb, vb, scale, causal=False, window=0)[0, :, 0, :]
+    return out

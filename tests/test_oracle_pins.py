@@ -1,0 +1,341 @@
+"""Pins of the float64 oracle to facts that do not come from the oracle itself.
+
+Each pin is chosen so that a plausible slip in ``oracle/`` (a dropped scale, a
+wrong mask sign or off-by-one, a transposed operand, the wrong GQA head, a
+softmax without the max shift, pages gathered in the wrong order) fails at
+least one test here:
+
+* brute force: a scalar pure-Python loop (math.exp / math.fsum) on tiny inputs;
+* closed forms: two-key softmax as a logistic function; position probes where
+  Q = 0 makes the weights uniform and V holds the bits of the key index, so
+  each output is a count of visible keys with a bit set, computed by formula;
+* special cases: a single key, causal row 0, window 1, identical keys, scale 0;
+* structure of the causal weight matrix printed on "拆开 LLM（二）" (section
+  "从对齐机器到 self-attention");
+* equivalences the pages state: GQA with Hkv = Hq is MHA, Hkv = 1 is MQA, both
+  equal attention over explicitly repeat_interleave'd K/V ("Attention 机制详解"
+  §5.2); a paged cache equals the contiguous one ("LLM 核心技术", section
+  PagedAttention); one decode step equals the matching row of a full causal
+  pass ("拆开 LLM（二）", section "KV cache");
+* the causality test of the LLMs-from-scratch article (gsyq.cn, §5): changing
+  future inputs leaves earlier outputs unchanged.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+
+
+# ----------------------------------------------------------------------------
+# brute force
+
+
+def _brute(q, k, v, scale, causal, window):
+    """Scalar loops over nested lists: q [B][Hq][Sq][D], k/v [B][Hkv][Sk][D]."""
+    B, Hq, Sq = len(q), len(q[0]), len(q[0][0])
+    Hkv, Sk, D = len(k[0]), len(k[0][0]), len(v[0][0][0])
+    group = Hq // Hkv
+    out = []
+    for b in range(B):
+        ob = []
+        for h in range(Hq):
+            g = h // group
+            oh = []
+            for i in range(Sq):
+                t = i + (Sk - Sq) + 1          # tokens 0 .. t-1 exist at row i
+                first = max(0, t - window) if window else 0
+                keys = list(range(first, t)) if causal else list(range(Sk))
+                logits = [math.fsum(q[b][h][i][c] * k[b][g][j][c] for c in range(D)) * scale
+                          for j in keys]
+                top = max(logits)
+                w = [math.exp(x - top) for x in logits]
+                z = math.fsum(w)
+                oh.append([math.fsum(w[n] * v[b][g][j][c] for n, j in enumerate(keys)) / z
+                           for c in range(D)])
+            ob.append(oh)
+        out.append(ob)
+    return np.array(out)
+
+
+CASES = [
+    # B, Hq, Hkv, Sq, Sk, D, causal, window
+    (1, 1, 1, 5, 5, 3, False, 0),
+    (2, 2, 1, 4, 6, 4, False, 0),
+    (1, 4, 2, 6, 6, 2, True, 0),
+    (2, 4, 4, 3, 7, 3, True, 0),      # Sq < Sk: bottom-right causal
+    (1, 2, 1, 7, 7, 4, True, 3),      # sliding window
+    (1, 4, 1, 8, 8, 2, True, 1),      # window of one key
+    (2, 2, 2, 2, 8, 3, True, 4),      # window with Sq < Sk
+    (1, 3, 3, 6, 6, 4, True, 9),      # window wider than the sequence
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_brute_force(case):
+    B, Hq, Hkv, Sq, Sk, D, causal, window = case
+    rng = np.random.default_rng(sum(case[:6]))
+    q = rng.standard_normal((B, Hq, Sq, D))
+    k = rng.standard_normal((B, Hkv, Sk, D))
+    v = rng.standard_normal((B, Hkv, Sk, D))
+    scale = 0.7
+    want = _brute(q.tolist(), k.tolist(), v.tolist(), scale, causal, window)
+    got = oracle.attention(q, k, v, scale, causal, window)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# closed forms
+
+
+def test_two_keys_is_logistic_even_when_exp_would_overflow():
+    # softmax over two logits a, b is (sigma(a - b), sigma(b - a)); with logits
+    # near 1000, exp without the max shift overflows to inf and gives NaN.
+    q = np.array([[[[1.0, 2.0]]]])
+    k = np.array([[[[300.0, 250.0], [310.0, 244.0]]]])
+    v = np.array([[[[1.0, -3.0], [5.0, 7.0]]]])
+    scale = 1.25
+    a = scale * (300.0 + 500.0)
+    b = scale * (310.0 + 488.0)
+    p0 = 1.0 / (1.0 + math.exp(b - a))
+    want = p0 * v[0, 0, 0] + (1.0 - p0) * v[0, 0, 1]
+    got = oracle.attention(q, k, v, scale)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_allclose(got[0, 0, 0], want, rtol=0, atol=1e-12)
+
+
+def _count_bit_below(n, c):
+    """#{0 <= j < n : bit c of j is 1}: full periods of 2^(c+1) plus the tail."""
+    period = 1 << (c + 1)
+    return (n // period) * (1 << c) + max(0, n % period - (1 << c))
+
+
+def _probe_expected(Sq, Sk, causal, window, nbits):
+    """O[i, c] for Q = 0 and V[j, c] = bit c of j, by counting."""
+    out = np.zeros((Sq, nbits))
+    for i in range(Sq):
+        t = i + (Sk - Sq) + 1 if causal else Sk
+        first = max(0, t - window) if window else 0
+        for c in range(nbits):
+            ones = _count_bit_below(t, c) - _count_bit_below(first, c)
+            out[i, c] = ones / (t - first)
+    return out
+
+
+@pytest.mark.parametrize("Sq,Sk,causal,window", [
+    (37, 37, False, 0), (37, 37, True, 0), (20, 45, True, 0),
+    (64, 64, True, 5), (30, 70, True, 16), (50, 50, True, 1), (50, 50, True, 200),
+])
+def test_position_probe(Sq, Sk, causal, window):
+    nbits = 7
+    q = np.zeros((1, 1, Sq, nbits))
+    k = np.random.default_rng(1).standard_normal((1, 1, Sk, nbits))
+    j = np.arange(Sk)
+    v = ((j[:, None] >> np.arange(nbits)[None, :]) & 1).astype(np.float64)[None, None]
+    got = oracle.attention(q, k, v, 0.3, causal, window)[0, 0]
+    np.testing.assert_allclose(got, _probe_expected(Sq, Sk, causal, window, nbits), atol=1e-12)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 4), (8, 2), (8, 1), (6, 3)])
+def test_gqa_head_mapping_probe(Hq, Hkv):
+    # V's last column holds the K/V head index, so it comes out unchanged for
+    # every query row; the expected head follows repeat_interleave order.
+    rng = np.random.default_rng(2)
+    S, D = 9, 4
+    q = rng.standard_normal((1, Hq, S, D))
+    k = rng.standard_normal((1, Hkv, S, D))
+    v = rng.standard_normal((1, Hkv, S, D))
+    v[..., -1] = np.arange(Hkv)[None, :, None]
+    order = np.repeat(np.arange(Hkv), Hq // Hkv)
+    got = oracle.attention(q, k, v, 0.5, causal=True)
+    np.testing.assert_allclose(got[0, :, :, -1], np.broadcast_to(order[:, None], (Hq, S)), atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# special cases
+
+
+def test_special_cases():
+    rng = np.random.default_rng(3)
+    S, D = 12, 5
+    q = rng.standard_normal((1, 1, S, D))
+    k = rng.standard_normal((1, 1, S, D))
+    v = rng.standard_normal((1, 1, S, D))
+    # one key: the output is that key's value
+    got = oracle.attention(q, k[:, :, :1], v[:, :, :1], 0.9)
+    np.testing.assert_allclose(got[0, 0], np.broadcast_to(v[0, 0, 0], (S, D)), atol=1e-12)
+    # causal row 0 sees only key 0
+    got = oracle.attention(q, k, v, 0.9, causal=True)
+    np.testing.assert_array_equal(got[0, 0, 0], v[0, 0, 0])
+    # a window of one key returns V row by row
+    got = oracle.attention(q, k, v, 0.9, causal=True, window=1)
+    np.testing.assert_array_equal(got[0, 0], v[0, 0])
+    # identical keys, scale 0 and Q = 0 all give the mean of the visible values
+    want = np.cumsum(v[0, 0], axis=0) / np.arange(1, S + 1)[:, None]
+    same_k = np.broadcast_to(k[:, :, :1], k.shape)
+    for got in (oracle.attention(q, same_k, v, 0.9, causal=True),
+                oracle.attention(q, k, v, 0.0, causal=True),
+                oracle.attention(np.zeros_like(q), k, v, 0.9, causal=True)):
+        np.testing.assert_allclose(got[0, 0], want, atol=1e-12)
+
+
+def test_softmax_rows_definition():
+    x = np.array([[0.0, -np.inf, 1.0], [1000.0, 999.0, -np.inf]])
+    p = oracle.softmax_rows(x)
+    assert p[0, 1] == 0.0 and p[1, 2] == 0.0
+    e = math.e
+    np.testing.assert_allclose(p[0], [1 / (1 + e), 0.0, e / (1 + e)], atol=1e-15)
+    np.testing.assert_allclose(p[1], [e / (1 + e), 1 / (1 + e), 0.0], atol=1e-15)
+
+
+def test_weight_matrix_structure_matches_printed_example():
+    path = __file__.replace("test_oracle_pins.py", "golden/p5_causal_weights_6x6.txt")
+    printed = np.loadtxt(path, comments="#")
+    assert printed.shape == (6, 6)
+    rng = np.random.default_rng(4)
+    q, k = rng.standard_normal((6, 8)), rng.standard_normal((6, 8))
+    w = oracle.attention_weights(q, k, 1 / math.sqrt(8), causal=True)
+    np.testing.assert_array_equal(w == 0.0, printed == 0.0)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, atol=1e-12)
+    np.testing.assert_allclose(printed.sum(axis=1), 1.0, atol=0.015)
+    # masking with 0 instead of -inf, or after the softmax, breaks one of these
+    assert np.all(w[np.tril_indices(6)] > 0)
+
+
+# ----------------------------------------------------------------------------
+# equivalences
+
+
+def test_gqa_equals_mha_and_mqa_on_repeated_kv():
+    rng = np.random.default_rng(5)
+    B, Hq, S, D = 2, 6, 10, 4
+    q = rng.standard_normal((B, Hq, S, D))
+    for Hkv in (6, 3, 2, 1):
+        k = rng.standard_normal((B, Hkv, S, D))
+        v = rng.standard_normal((B, Hkv, S, D))
+        rep = Hq // Hkv
+        kk, vv = np.repeat(k, rep, axis=1), np.repeat(v, rep, axis=1)
+        np.testing.assert_allclose(oracle.attention(q, k, v, 0.4, causal=True),
+                                   oracle.attention(q, kk, vv, 0.4, causal=True), atol=1e-13)
+
+
+def test_rows_and_chunks_match_full():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((2, 4, 33, 8))
+    k = rng.standard_normal((2, 2, 40, 8))
+    v = rng.standard_normal((2, 2, 40, 8))
+    full = oracle.attention(q, k, v, 0.3, causal=True, window=9)
+    np.testing.assert_allclose(oracle.attention(q, k, v, 0.3, causal=True, window=9, row_chunk=5),
+                               full, atol=1e-14)
+    rows = [0, 7, 32, 15]
+    np.testing.assert_allclose(oracle.attention_rows(q, k, v, 1, 3, rows, 0.3, True, 9),
+                               full[1, 3, rows], atol=1e-14)
+
+
+def test_bottom_right_alignment_matches_square_pass():
+    rng = np.random.default_rng(7)
+    S, m, D = 20, 6, 5
+    q = rng.standard_normal((1, 2, S, D))
+    k = rng.standard_normal((1, 1, S, D))
+    v = rng.standard_normal((1, 1, S, D))
+    for window in (0, 4):
+        full = oracle.attention(q, k, v, 0.8, causal=True, window=window)
+        tail = oracle.attention(q[:, :, S - m:], k, v, 0.8, causal=True, window=window)
+        np.testing.assert_allclose(tail, full[:, :, S - m:], atol=1e-14)
+
+
+def _paged_from_contiguous(kc, vc, lens, page_size, rng, permute):
+    """Scatter contiguous [B, Hkv, Smax, D] caches into a shuffled page pool."""
+    counts = [(n + page_size - 1) // page_size for n in lens]
+    total = sum(counts)
+    perm = rng.permutation(total) if permute else np.arange(total)
+    Hkv, D = kc.shape[1], kc.shape[3]
+    kp = np.full((total, Hkv, page_size, D), np.nan)
+    vp = np.full((total, Hkv, page_size, D), np.nan)
+    entry = 0
+    for b, n in enumerate(lens):
+        for t in range(n):
+            page = perm[entry + t // page_size]
+            kp[page, :, t % page_size] = kc[b, :, t]
+            vp[page, :, t % page_size] = vc[b, :, t]
+        entry += counts[b]
+    return kp, vp, perm.astype(np.int32)
+
+
+@pytest.mark.parametrize("permute", [False, True])
+def test_paged_equals_contiguous(permute):
+    rng = np.random.default_rng(8)
+    lens = [1, 16, 17, 40, 5]
+    B, Hq, Hkv, D, ps = len(lens), 4, 2, 6, 8
+    Smax = max(lens)
+    kc = rng.standard_normal((B, Hkv, Smax, D))
+    vc = rng.standard_normal((B, Hkv, Smax, D))
+    q = rng.standard_normal((B, Hq, D))
+    kp, vp, table = _paged_from_contiguous(kc, vc, lens, ps, rng, permute)
+    got = oracle.decode_paged(q, kp, vp, table, np.array(lens), ps, 0.6)
+    assert np.all(np.isfinite(got))  # NaN padding is never read
+    for b, n in enumerate(lens):
+        want = oracle.attention(q[b][None, :, None, :], kc[b:b + 1, :, :n], vc[b:b + 1, :, :n], 0.6)
+        np.testing.assert_allclose(got[b], want[0, :, 0, :], atol=1e-13)
+
+
+def test_paged_position_probe():
+    # V slot of logical token t holds the bits of t; Q = 0 -> mean of bits.
+    rng = np.random.default_rng(9)
+    lens, ps, nbits = [3, 16, 33, 100], 16, 7
+    B, Hkv = len(lens), 2
+    Smax = max(lens)
+    kc = rng.standard_normal((B, Hkv, Smax, nbits))
+    bits = ((np.arange(Smax)[:, None] >> np.arange(nbits)[None, :]) & 1).astype(np.float64)
+    vc = np.broadcast_to(bits, (B, Hkv, Smax, nbits)).copy()
+    kp, vp, table = _paged_from_contiguous(kc, vc, lens, ps, rng, True)
+    got = oracle.decode_paged(np.zeros((B, 4, nbits)), kp, vp, table, np.array(lens), ps, 1.0)
+    for b, n in enumerate(lens):
+        want = [_count_bit_below(n, c) / n for c in range(nbits)]
+        np.testing.assert_allclose(got[b], np.broadcast_to(want, (4, nbits)), atol=1e-12)
+
+
+def test_incremental_decode_equals_full_recompute():
+    rng = np.random.default_rng(10)
+    n, Hq, Hkv, D, ps = 21, 4, 2, 5, 4
+    q = rng.standard_normal((1, Hq, n, D))
+    k = rng.standard_normal((1, Hkv, n, D))
+    v = rng.standard_normal((1, Hkv, n, D))
+    full = oracle.attention(q, k, v, 0.5, causal=True)
+    for t in range(1, n + 1):
+        kp, vp, table = _paged_from_contiguous(k, v, [t], ps, rng, True)
+        step = oracle.decode_paged(q[:, :, t - 1], kp, vp, table, np.array([t]), ps, 0.5)
+        np.testing.assert_allclose(step[0], full[0, :, t - 1], atol=1e-13)
+
+
+@pytest.mark.parametrize("window", [0, 3])
+def test_future_perturbation_leaves_past_rows_unchanged(window):
+    # gsyq.cn article §5: add 10 to every input after position 2; the outputs
+    # of the first positions must not move. Here K and V after (and, with a
+    # window, long before) each probed row are perturbed.
+    rng = np.random.default_rng(11)
+    S, D = 12, 6
+    q = rng.standard_normal((1, 3, S, D))
+    k = rng.standard_normal((1, 3, S, D))
+    v = rng.standard_normal((1, 3, S, D))
+    base = oracle.attention(q, k, v, 0.5, causal=True, window=window)
+    for i in (0, 2, 7):
+        k2, v2 = k.copy(), v.copy()
+        k2[:, :, i + 1:] += 10.0
+        v2[:, :, i + 1:] += 10.0
+        if window:
+            k2[:, :, :max(0, i - window + 1)] -= 10.0
+            v2[:, :, :max(0, i - window + 1)] -= 10.0
+        pert = oracle.attention(q, k2, v2, 0.5, causal=True, window=window)
+        np.testing.assert_array_equal(pert[:, :, i], base[:, :, i])
+
+
+def test_visible_rejects_window_without_causal():
+    with pytest.raises(ValueError):
+        oracle.visible(4, 4, causal=False, window=2)
+
+
+def test_sequence_pages_layout():
+    assert oracle.sequence_pages([1, 16, 17, 32], 16) == [(0, 1), (1, 1), (2, 2), (4, 2)]
