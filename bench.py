@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Throughput of the attention hot path on one MI355X.
+
+One step = one causal GQA prefill (B=4, Sq=Sk=4096, Hq=32, Hkv=8, D=128, bf16)
+followed by one paged GQA decode step (64 sequences, lengths uniform in
+[512, 8192], Hq=32, Hkv=8, D=128, page_size 16, bf16). Inputs are seeded
+synthetic N(0,1) tensors already resident in HBM.
+
+Printed: ONE JSON line on stdout. ``value`` is prefill attention TFLOP/s
+(4·D flop per visible query/key pair) from HIP events around each prefill
+launch; the decode step's KV GB/s (every cached K/V byte once) is reported
+under ``decode``; ``roofline`` is the prefill kernel against the MI355X dense
+bf16 MFMA peak. ``cpu_baseline`` times the float64 oracle on a bounded sample
+of the prefill workload on the host cores. Progress goes to stderr.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill attn TFLOP/s + paged-decode KV GB/s, fraction of MI355X peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PREFILL = "gqa_causal_4k"
+DECODE = "paged_decode"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _traffic(kernel_key, source_file):
+    """HBM bytes per launch from the committed PMC summary, if the kernel's
+    source is unchanged since those counters were taken; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)[kernel_key]
+        with open(source_file, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(q, k, v, scale, seconds):
+    """Time the float64 oracle on whole (batch, head) units of the prefill
+    workload until `seconds` have passed; report TFLOP/s on the same
+    visible-pair count the GPU figure uses."""
+    import numpy as np
+
+    import oracle
+    from scaled_dot_product_flash_amd import work
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    qn, kn, vn = (t.float().numpy() for t in (q, k, v))
+    B, Hq, Sq, D = qn.shape
+    Sk = kn.shape[2]
+    units = [(b, h) for b in range(B) for h in range(Hq)]
+    np.random.default_rng(0).shuffle(units)
+    rows = np.arange(Sq)
+    per_unit = work.attention_flops(work.visible_pairs(Sq, Sk, True, 0), D)
+    done = 0
+    t0 = time.perf_counter()
+    for b, h in units:
+        out = oracle.attention_rows(qn, kn, vn, b, h, rows, scale, True, 0)
+        assert np.isfinite(out).all()
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {
+        "value": round(done * per_unit / el / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {len(units)} (batch, query head) units of the causal GQA prefill workload, "
+                  f"all {Sq} query rows each, float64 numpy, {el:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="add one plain 256 MiB device copy per step (byte-counter scale for PMC runs)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the kernels run on one GPU's "
+              "share; see the sharding note in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import scaled_dot_product_flash_amd as attn
+    from scaled_dot_product_flash_amd import inputs, work
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    attn.load_library()
+
+    wp, wd = inputs.WORKLOADS[PREFILL], inputs.WORKLOADS[DECODE]
+    log("generating inputs")
+    q, k, v = inputs.workload_inputs(PREFILL)
+    dd = inputs.workload_inputs(DECODE)
+    pq, pk, pv = (t.to(dev) for t in (q, k, v))
+    po = torch.empty_like(pq)
+    dq, dkp, dvp, dpt, dsl = (dd[n].to(dev) for n in ("q", "k_pool", "v_pool", "page_table", "seq_lens"))
+    do = torch.empty_like(dq)
+    p_scale = 1.0 / math.sqrt(wp["D"])
+    d_scale = 1.0 / math.sqrt(wd["D"])
+    if args.copy_calibration:
+        csrc = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        cdst = torch.empty_like(csrc)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        attn.fwd(pq, pk, pv, o=po, scale=p_scale, causal=True, window=0)
+        if ev is not None:
+            ev[1].record()
+        attn.decode_paged(dq, dkp, dvp, dpt, dsl, scale=d_scale, o=do)
+        if ev is not None:
+            ev[2].record()
+        if args.copy_calibration:
+            cdst.copy_(csrc)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [e[0].elapsed_time(e[1]) for e in events]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in events]
+    assert torch.isfinite(po.float()).all() and torch.isfinite(do.float()).all()
+    log("timing done")
+
+    import statistics
+
+    p_flops = work.prefill_flops(wp["B"], wp["Hq"], wp["Sq"], wp["Sk"], wp["D"], True, 0)
+    d_bytes = work.decode_kv_bytes(dd["seq_lens"].tolist(), wd["Hkv"], wd["D"], 2)
+    p_mean = statistics.fmean(pre_ms)
+    d_mean = statistics.fmean(dec_ms)
+    p_tflops = p_flops / (p_mean * 1e-3) / 1e12
+    d_gbps = d_bytes / (d_mean * 1e-3) / 1e9
+    csrc_dir = os.path.join(ROOT, "scaled_dot_product_flash_amd", "csrc")
+
+    out = {
+        "metric": METRIC,
+        "value": round(p_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal GQA prefill B=4 Sq=Sk=4096 Hq=32 Hkv=8 D=128 + paged GQA decode "
+                        "64 seqs len~U[512,8192] Hq=32 Hkv=8 D=128 page_size=16",
+            "prefill": {"B": wp["B"], "Hq": wp["Hq"], "Hkv": wp["Hkv"], "Sq": wp["Sq"], "Sk": wp["Sk"],
+                        "D": wp["D"], "causal": True, "window": 0, "flop_per_call": p_flops},
+            "decode": {"seqs": wd["nseq"], "Hq": wd["Hq"], "Hkv": wd["Hkv"], "D": wd["D"],
+                       "page_size": wd["page_size"], "tokens": int(dd["seq_lens"].sum()),
+                       "kv_bytes_per_call": d_bytes},
+            "parallelism": "single GPU",
+        },
+        "prefill": {"ms_mean": round(p_mean, 5), "ms_median": round(statistics.median(pre_ms), 5),
+                    "ms_min": round(min(pre_ms), 5), "tflops": round(p_tflops, 3),
+                    "frac_peak": round(p_tflops / PEAK_BF16_TFLOPS, 4)},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(p_tflops, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": _traffic("prefill_bf16_kernel", os.path.join(csrc_dir, "prefill_bf16.hip")),
+        },
+        "decode": {
+            "value": round(d_gbps, 2),
+            "unit": "GB/s",
+            "ms_mean": round(d_mean, 5),
+            "ms_median": round(statistics.median(dec_ms), 5),
+            "ms_min": round(min(dec_ms), 5),
+            "roofline": {
+                "bound": "hbm",
+                "achieved": round(d_gbps, 2),
+                "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s",
+                "frac": round(d_gbps / PEAK_HBM_GBPS, 4),
+                "traffic": _traffic("decode_split_kernel", os.path.join(csrc_dir, "decode_paged.hip")),
+            },
+        },
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline (~{args.cpu_seconds:.0f} s of oracle work)")
+        out["cpu_baseline"] = cpu_baseline(q, k, v, p_scale, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

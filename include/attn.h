@@ -1,0 +1,136 @@
+/*
+ * attn.h — C ABI of libattn.so: fused scaled-dot-product attention on MI355X
+ * (gfx950), prefill and paged single-token decode.
+ *
+ * The operation (web pages, cited by title and section):
+ *   O = softmax(Q K^T * scale) V, row by row, with masked logits set to -inf
+ *   before the softmax and the row maximum subtracted before exponentiating
+ *   ("Attention 机制详解：从 Self-Attention 到 Multi-Query Attention" §2.1–2.2;
+ *   "拆开 LLM（二）：手撕注意力", sections "手撕三种打分函数" and
+ *   "从对齐机器到 self-attention"). It is computed tile by tile with an online
+ *   softmax so the Sq x Sk score matrix never reaches memory ("Attention 机制
+ *   详解" §7; "拆开 LLM（二）", section on FlashAttention: the result is exact,
+ *   not an approximation).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller, dense and
+ *     row-major in the layout stated per call, 16-byte aligned. The library
+ *     never frees or retains them.
+ *   - Calls are asynchronous: they validate the arguments on the host (before
+ *     any HIP call, so every error below is reported without touching a GPU),
+ *     enqueue kernels on `stream` and return. Faults inside a kernel surface
+ *     at the caller's next synchronisation of that stream.
+ *   - Return value: ATTN_OK (0) or a negative ATTN_ERR_* code; nothing is
+ *     enqueued when an error is returned. No C++ exception crosses the ABI.
+ *   - GQA/MQA: Hq must be a multiple of Hkv; query head h reads K/V head
+ *     h / (Hq / Hkv) ("Attention 机制详解" §5.2, repeat_interleave order).
+ *     Hkv == Hq is plain multi-head attention, Hkv == 1 is multi-query.
+ *   - A zero batch (B == 0), or Sq == 0 for prefill, is a valid empty call.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = -1,     /* a required pointer is NULL */
+    ATTN_ERR_SHAPE = -2,    /* a size is negative or zero where it must be >= 1,
+                               causal with Sq > Sk, or an element count
+                               overflows 64-bit addressing */
+    ATTN_ERR_HEADS = -3,    /* Hq < 1, Hkv < 1 or Hq % Hkv != 0 */
+    ATTN_ERR_HEADDIM = -4,  /* D is not 64 or 128 */
+    ATTN_ERR_MASK = -5,     /* causal not 0/1, window < 0, or window > 0 without causal */
+    ATTN_ERR_SCALE = -6,    /* scale is NaN or infinite */
+    ATTN_ERR_PAGE = -7,     /* page_size is not a power of two in [8, 256] */
+    ATTN_ERR_ALIGN = -8,    /* a tensor pointer is not 16-byte aligned */
+    ATTN_ERR_NOMEM = -9,    /* the decode workspace could not be allocated */
+    ATTN_ERR_HIP = -10      /* a HIP runtime call or kernel launch failed */
+};
+
+/*
+ * attn_fwd — prefill attention, bfloat16 in and out, float32 accumulation.
+ *
+ *   q, o : [B, Hq, Sq, D] bfloat16      k, v : [B, Hkv, Sk, D] bfloat16
+ *   scale: multiplies Q K^T (typically 1/sqrt(D), "Attention 机制详解" §2.1);
+ *          any finite value, 0 gives the mean of the visible V rows.
+ *   causal: 1 = each query sees only keys at or before its position
+ *          ("拆开 LLM（二）", causal mask = lower triangle). When Sq < Sk the
+ *          queries are the LAST Sq positions: row i sits at position
+ *          i + Sk - Sq (bottom-right alignment, which makes a one-token call
+ *          equal to one decode step over a cache of Sk tokens).
+ *   window: 0 = no window; W > 0 (requires causal) = each query sees only the
+ *          W most recent keys, its own position included ("LLM 核心技术：
+ *          Attention 机制的实现与优化", sliding-window section; "拆开 LLM（二）",
+ *          exercise keeping the last 256 cache entries).
+ *   The probabilities P are rounded to bfloat16 before P·V; O is rounded to
+ *   bfloat16 (round-to-nearest-even) once, after the final normalisation.
+ *   o must not overlap q, k or v.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o,
+             int B, int Hq, int Hkv, int Sq, int Sk, int D,
+             float scale, int causal, int window, hipStream_t stream);
+
+/*
+ * attn_fwd_f32 — the same operation and arguments with float32 tensors and
+ * float32 arithmetic throughout (no reduced-precision rounding of Q, K, P or
+ * V). Intended for accuracy checks against a float64 reference.
+ */
+int attn_fwd_f32(const void* q, const void* k, const void* v, void* o,
+                 int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                 float scale, int causal, int window, hipStream_t stream);
+
+/*
+ * attn_decode_paged — one decode step: each of B sequences has one new query
+ * token that attends, without a mask, to every token of its paged KV cache
+ * ("拆开 LLM（二）", KV-cache section: the new token's k and v are appended
+ * first, then it attends over all cached positions; "LLM 核心技术",
+ * PagedAttention section: the cache is stored in fixed-size pages of a global
+ * pool and reached through a page table).
+ *
+ *   q, o        : [B, Hq, D] bfloat16, one token per sequence.
+ *   k_pool,
+ *   v_pool      : [num_pages, Hkv, page_size, D] bfloat16; each (page, head)
+ *                 is one contiguous page_size x D tile.
+ *   seq_lens    : [B] int32, device memory: tokens cached for sequence b,
+ *                 the current token included; every entry must be >= 1.
+ *   page_table  : int32, device memory, ragged: sequence b owns the
+ *                 ceil(seq_lens[b] / page_size) consecutive entries starting
+ *                 at off_b = sum over j < b of ceil(seq_lens[j] / page_size);
+ *                 entry off_b + p is the physical page of logical page p.
+ *                 Token t of sequence b is slot t % page_size of logical page
+ *                 t / page_size. Slots at or past seq_lens[b] are never read
+ *                 (they may hold anything, NaN included).
+ *   page_size   : power of two in [8, 256].
+ *   Device-side preconditions the host cannot check without synchronising:
+ *   seq_lens[b] >= 1 and every used page id in [0, num_pages); violating
+ *   them is undefined behaviour.
+ *   The split-context partial results live in a library-owned workspace,
+ *   allocated on first use per (device, stream) and grown as needed; calls on
+ *   different streams never share a workspace. P is rounded to bfloat16
+ *   before P·V, as in attn_fwd.
+ */
+int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* page_table, const int32_t* seq_lens,
+                      int B, int Hq, int Hkv, int D, int page_size,
+                      float scale, void* o, hipStream_t stream);
+
+/* attn_strerror — static, never-NULL description of a status code. */
+const char* attn_strerror(int status);
+
+/*
+ * attn_release — synchronise every device the library used and free the
+ * decode workspaces. Idempotent; later calls allocate again on demand.
+ */
+void attn_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

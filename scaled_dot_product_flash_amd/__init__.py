@@ -1,0 +1,160 @@
+"""Python binding of libattn.so (MI355X / gfx950 fused attention).
+
+Argument marshalling only: each function checks that the tensors have the
+dtype, device, layout and shapes the C ABI expects, passes their device
+pointers and torch's current HIP stream, and raises ``RuntimeError`` with the
+library's message when a call returns an error. Every arithmetic step runs in
+the library's kernels; there is no fallback path. If ``libattn.so`` has not
+been built the first call raises.
+
+The C ABI is declared in ``include/attn.h``.
+"""
+
+import ctypes
+import math
+import os
+
+__all__ = ["fwd", "fwd_f32", "decode_paged", "strerror", "release", "library_path", "load_library"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+ATTN_OK = 0
+
+
+def library_path():
+    return os.path.join(_HERE, "libattn.so")
+
+
+def load_library():
+    """Load libattn.so once. torch is imported first so the library binds to
+    the HIP runtime torch already uses (one runtime per process)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    import torch  # noqa: F401  (loads torch's libamdhip64 before ours)
+
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m scaled_dot_product_flash_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    for name in ("attn_fwd", "attn_fwd_f32"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
+        fn.restype = i32
+    lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp]
+    lib.attn_decode_paged.restype = i32
+    lib.attn_strerror.argtypes = [i32]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_release.argtypes = []
+    lib.attn_release.restype = None
+    _LIB = lib
+    return lib
+
+
+def strerror(code):
+    return load_library().attn_strerror(int(code)).decode()
+
+
+def release():
+    load_library().attn_release()
+
+
+def _check(rc, what):
+    if rc != ATTN_OK:
+        raise RuntimeError(f"{what} failed ({rc}): {strerror(rc)}")
+
+
+def _stream(t):
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name, dtype):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _prefill(entry, dtype, q, k, v, o, scale, causal, window):
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, dtype)
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, S, D]")
+    B, Hq, Sq, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", dtype)
+    if o.shape != q.shape:
+        raise ValueError("o must have the shape of q")
+    if not (q.device == k.device == v.device == o.device):
+        raise ValueError("all tensors must be on one device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    with torch.cuda.device(q.device):
+        rc = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, Hq, Hkv, Sq, Sk, D,
+                   float(scale), int(bool(causal)), int(window), _stream(q))
+    _check(rc, entry.__name__)
+    return o
+
+
+def fwd(q, k, v, o=None, scale=None, causal=False, window=0):
+    """bf16 prefill attention: q [B,Hq,Sq,D], k/v [B,Hkv,Sk,D] -> o [B,Hq,Sq,D]."""
+    import torch
+
+    return _prefill(load_library().attn_fwd, torch.bfloat16, q, k, v, o, scale, causal, window)
+
+
+def fwd_f32(q, k, v, o=None, scale=None, causal=False, window=0):
+    """float32 prefill attention with float32 arithmetic throughout."""
+    import torch
+
+    return _prefill(load_library().attn_fwd_f32, torch.float32, q, k, v, o, scale, causal, window)
+
+
+def decode_paged(q, k_pool, v_pool, page_table, seq_lens, scale=None, o=None):
+    """One decode step over a paged cache.
+
+    q [B,Hq,D] bf16; k_pool / v_pool [num_pages,Hkv,page_size,D] bf16;
+    page_table int32 (ragged, see include/attn.h); seq_lens [B] int32.
+    """
+    import torch
+
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    _need(k_pool, "k_pool", torch.bfloat16)
+    _need(v_pool, "v_pool", torch.bfloat16)
+    _need(page_table, "page_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    if q.dim() != 3 or k_pool.dim() != 4 or k_pool.shape != v_pool.shape:
+        raise ValueError("q must be [B,Hq,D] and the pools [num_pages,Hkv,page_size,D]")
+    B, Hq, D = q.shape
+    Hkv, ps = k_pool.shape[1], k_pool.shape[2]
+    if k_pool.shape[3] != D or seq_lens.shape != (B,):
+        raise ValueError("pool head dim or seq_lens length does not match q")
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", torch.bfloat16)
+    if o.shape != q.shape:
+        raise ValueError("o must have the shape of q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    with torch.cuda.device(q.device):
+        rc = lib.attn_decode_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(),
+                                   seq_lens.data_ptr(), B, Hq, Hkv, D, ps, float(scale), o.data_ptr(), _stream(q))
+    _check(rc, "attn_decode_paged")
+    return o

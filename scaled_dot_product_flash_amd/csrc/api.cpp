@@ -1,0 +1,179 @@
+// C ABI of libattn.so: argument validation, dispatch, decode workspace.
+// Every argument is checked on the host before the first HIP call, so each
+// error code is reachable without a GPU.
+
+#include "attn.h"
+#include "launch.h"
+
+#include <cmath>
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <utility>
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// a*b*c*d fits in int64 (all factors >= 0)
+bool product_fits(long long a, long long b, long long c, long long d) {
+    const unsigned __int128 p = (unsigned __int128)a * b * c * d;
+    return p < ((unsigned __int128)1 << 62);
+}
+
+int validate_prefill(const void* q, const void* k, const void* v, const void* o, int B, int Hq, int Hkv,
+                     int Sq, int Sk, int D, float scale, int causal, int window, bool* empty) {
+    *empty = false;
+    if (B < 0 || Sq < 0) return ATTN_ERR_SHAPE;
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_HEADS;
+    if (D != 64 && D != 128) return ATTN_ERR_HEADDIM;
+    if (causal != 0 && causal != 1) return ATTN_ERR_MASK;
+    if (window < 0 || (window > 0 && !causal)) return ATTN_ERR_MASK;
+    if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+    if (B == 0 || Sq == 0) {
+        *empty = true;
+        return ATTN_OK;
+    }
+    if (Sk < 1) return ATTN_ERR_SHAPE;
+    if (causal && Sq > Sk) return ATTN_ERR_SHAPE;
+    if (!product_fits(B, Hq, Sq, D) || !product_fits(B, Hkv, Sk, D)) return ATTN_ERR_SHAPE;
+    // grid of either kernel (at most one workgroup per 64 rows, rounded to 8)
+    const long long items = (long long)B * Hq * ((Sq + 63) / 64) + 8;
+    if (items > 0x7FFFFFFFLL) return ATTN_ERR_SHAPE;
+    if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
+    return ATTN_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+// ---- decode workspace: one buffer per (device, stream), grown on demand ----
+
+struct Workspace {
+    float* ptr = nullptr;
+    size_t floats = 0;
+};
+
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::map<int, int> g_cu_count;
+
+int get_workspace(int device, hipStream_t stream, size_t floats, float** out) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace& w = g_ws[{device, stream}];
+    if (w.floats < floats) {
+        if (w.ptr) {
+            // earlier calls on this stream may still read the old buffer
+            if (hipStreamSynchronize(stream) != hipSuccess) return ATTN_ERR_HIP;
+            if (hipFree(w.ptr) != hipSuccess) return ATTN_ERR_HIP;
+            w.ptr = nullptr;
+            w.floats = 0;
+        }
+        void* p = nullptr;
+        if (hipMalloc(&p, floats * sizeof(float)) != hipSuccess || !p) return ATTN_ERR_NOMEM;
+        w.ptr = static_cast<float*>(p);
+        w.floats = floats;
+    }
+    *out = w.ptr;
+    return ATTN_OK;
+}
+
+int cu_count(int device, int* out) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    auto it = g_cu_count.find(device);
+    if (it == g_cu_count.end()) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+            return ATTN_ERR_HIP;
+        it = g_cu_count.emplace(device, n).first;
+    }
+    *out = it->second;
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Sq, int Sk,
+             int D, float scale, int causal, int window, hipStream_t stream) {
+    bool empty = false;
+    const int rc = validate_prefill(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, &empty);
+    if (rc != ATTN_OK || empty) return rc;
+    attn::PrefillArgs a{q, k, v, o, B, Hq, Hkv, Sq, Sk, D, scale, causal, window};
+    return hip_status(attn::launch_prefill_bf16(a, stream));
+}
+
+int attn_fwd_f32(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Sq,
+                 int Sk, int D, float scale, int causal, int window, hipStream_t stream) {
+    bool empty = false;
+    const int rc = validate_prefill(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, &empty);
+    if (rc != ATTN_OK || empty) return rc;
+    attn::PrefillArgs a{q, k, v, o, B, Hq, Hkv, Sq, Sk, D, scale, causal, window};
+    return hip_status(attn::launch_prefill_f32(a, stream));
+}
+
+int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                      const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int page_size, float scale,
+                      void* o, hipStream_t stream) {
+    if (B < 0) return ATTN_ERR_SHAPE;
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_HEADS;
+    if (D != 64 && D != 128) return ATTN_ERR_HEADDIM;
+    if (page_size < 8 || page_size > 256 || (page_size & (page_size - 1)) != 0) return ATTN_ERR_PAGE;
+    if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+    if (B == 0) return ATTN_OK;
+    if (B > 65535 || Hq > 65535) return ATTN_ERR_SHAPE;
+    if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !o) return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o) || !aligned4(page_table) ||
+        !aligned4(seq_lens))
+        return ATTN_ERR_ALIGN;
+
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return ATTN_ERR_HIP;
+    int ncu = 0;
+    int rc = cu_count(device, &ncu);
+    if (rc != ATTN_OK) return rc;
+    const int nsplit = attn::decode_nsplit(B, Hq, Hkv, ncu);
+    float* ws = nullptr;
+    rc = get_workspace(device, stream, attn::decode_workspace_floats(B, Hq, D, nsplit), &ws);
+    if (rc != ATTN_OK) return rc;
+    attn::DecodeArgs a{q, k_pool, v_pool, page_table, seq_lens, o, B, Hq, Hkv, D, page_size, scale, nsplit, ws};
+    return hip_status(attn::launch_decode_paged(a, stream));
+}
+
+const char* attn_strerror(int status) {
+    switch (status) {
+        case ATTN_OK: return "success";
+        case ATTN_ERR_NULL: return "a required pointer is NULL";
+        case ATTN_ERR_SHAPE: return "invalid size (negative, zero where >= 1 is required, causal with Sq > Sk, or too large)";
+        case ATTN_ERR_HEADS: return "invalid head counts (need Hq >= 1, Hkv >= 1, Hq % Hkv == 0)";
+        case ATTN_ERR_HEADDIM: return "unsupported head dimension (D must be 64 or 128)";
+        case ATTN_ERR_MASK: return "invalid mask arguments (causal must be 0/1; window >= 0 and only with causal)";
+        case ATTN_ERR_SCALE: return "scale is not finite";
+        case ATTN_ERR_PAGE: return "page_size must be a power of two in [8, 256]";
+        case ATTN_ERR_ALIGN: return "a tensor pointer is not sufficiently aligned (16 bytes; 4 for int32 tables)";
+        case ATTN_ERR_NOMEM: return "device memory for the decode workspace could not be allocated";
+        case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+        default: return "unknown attn status code";
+    }
+}
+
+void attn_release(void) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    if (g_ws.empty()) return;
+    int prev = -1;
+    const bool have_prev = hipGetDevice(&prev) == hipSuccess;
+    for (auto& kv : g_ws) {
+        if (kv.second.ptr) {
+            if (hipSetDevice(kv.first.first) == hipSuccess) {
+                (void)hipDeviceSynchronize();
+                (void)hipFree(kv.second.ptr);
+            }
+        }
+    }
+    g_ws.clear();
+    if (have_prev) (void)hipSetDevice(prev);
+}
+
+}  // extern "C"

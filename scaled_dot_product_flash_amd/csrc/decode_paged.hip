@@ -1,0 +1,377 @@
+// Single-token decode over a paged KV cache, bfloat16, gfx950.
+//
+// What it computes: for each sequence b and query head h,
+//   o[b,h] = softmax(q[b,h] · K_b^T * scale) V_b
+// over every cached token 0 .. seq_lens[b]-1, with no mask ("拆开 LLM（二）：
+// 手撕注意力", KV-cache section: the new token attends to all cached
+// positions). K_b / V_b are not contiguous: token t of sequence b is slot
+// t % page_size of physical page page_table[off_b + t / page_size] of a
+// global pool ("LLM 核心技术：Attention 机制的实现与优化", PagedAttention
+// section; "Attention From Scratch", paged-KV-cache part: fixed-size pages, a
+// per-sequence page table and a global page pool).
+//
+// The step is bound by HBM bandwidth (every cached K/V byte is read once), so
+// the design is about bytes in flight and cheap per-byte VALU work, not MFMA:
+//  * Split kernel, grid (split, kv-head group, sequence). The query heads that
+//    share a K/V head (up to 8) are packed into one workgroup so each page is
+//    read once for all of them. The sequence's context is cut into `nsplit`
+//    contiguous runs of 16-token (D=128) or 32-token (D=64) blocks; the four
+//    waves of a workgroup take the run's blocks round-robin.
+//  * A block is read with four 16-byte loads per lane per tensor; lane l holds
+//    d-chunk l % (D/8) of token l / (D/8) (+ 4 or 8 per load), so every load
+//    instruction reads 1 KiB of one page contiguously. The next block's loads
+//    are issued before the current block is consumed.
+//  * q·k: bf16 pair dot products (v_dot2_f32_bf16) over the lane's 8 dims,
+//    then a DPP all-reduce over the lanes of the token.
+//  * Online softmax per lane row (the lanes that hold the same tokens): the
+//    running max / sum / output of a row only ever see that row's tokens, so
+//    the loop needs no cross-row traffic; rows, then waves, then splits are
+//    merged at the end with the same rescale rule the online softmax uses.
+//  * p·v: P is rounded to bf16 and paired over two tokens, V is re-paired over
+//    the same two tokens, and v_dot2_f32_bf16 accumulates both at once.
+//  * Tokens at or past seq_lens[b] are excluded by selection (logit -inf, V
+//    zeroed), never by multiplying with 0, so NaN padding cannot leak.
+//  * Merge kernel: per (sequence, query head) combines the split partials
+//    (m, l, o) into the bf16 output.
+
+#include "launch.h"
+
+#include <cmath>
+
+namespace attn {
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the lanes that hold one token: 16 lanes (a DPP row) for D = 128,
+// 8 lanes (half a row) for D = 64. Every lane of the group gets the sum.
+template <int CPT>
+__device__ __forceinline__ float token_sum(float x) {
+    if constexpr (CPT == 16) {
+        x += dpp<0x128>(x);  // row_ror:8
+        x += dpp<0x124>(x);  // row_ror:4
+        x += dpp<0x122>(x);  // row_ror:2
+        x += dpp<0x121>(x);  // row_ror:1
+    } else {
+        x += dpp<0x141>(x);  // row_half_mirror: lane i + lane 7-i
+        x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+        x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+    }
+    return x;
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+template <int D, int GH>
+__global__ __launch_bounds__(kThreads)
+void decode_split_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __restrict__ Kp,
+                         const uint16_t* __restrict__ Vp, const int32_t* __restrict__ table,
+                         const int32_t* __restrict__ lens, float* __restrict__ ws,
+                         int Hq, int Hkv, int ps_log2, int nsplit, float c2) {
+    constexpr int CPT = D / 8;        // lanes per token (16-byte chunks per row)
+    constexpr int TPI = 64 / CPT;     // tokens per load instruction
+    constexpr int TB = 4 * TPI;       // tokens per block
+
+    __shared__ float sh_m[kWaves][GH];
+    __shared__ float sh_l[kWaves][GH];
+    __shared__ __attribute__((aligned(16))) float sh_o[kWaves][GH][D];
+    __shared__ int sh_red[kWaves];
+
+    const int split = blockIdx.x;
+    const int hgrp = blockIdx.y;        // (kv head, head group)
+    const int b = blockIdx.z;
+    const int G = Hq / Hkv;
+    const int groups_per_kv = G / GH;
+    const int g = hgrp / groups_per_kv;
+    const int h0 = g * G + (hgrp % groups_per_kv) * GH;
+    const int ps = 1 << ps_log2;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int c = lane % CPT;
+    const int r = lane / CPT;
+
+    // off_b = sum_{j<b} ceil(len_j / ps), the sequence's first page-table entry
+    int part = 0;
+    for (int j = tid; j < b; j += kThreads) part += (lens[j] + ps - 1) >> ps_log2;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
+    if (lane == 0) sh_red[wave] = part;
+    __syncthreads();
+    const int off_b = sh_red[0] + sh_red[1] + sh_red[2] + sh_red[3];
+    const int len = lens[b];
+    const int32_t* tab = table + off_b;
+
+    const int nblk = (len + TB - 1) / TB;
+    const int blk_begin = (int)((long long)nblk * split / nsplit);
+    const int blk_end = (int)((long long)nblk * (split + 1) / nsplit);
+
+    // q of the packed heads: 8 dims (4 bf16 pairs) per lane and head
+    uint32_t qv[GH][4];
+#pragma unroll
+    for (int j = 0; j < GH; ++j) {
+        const uint4 x = ld16(Qp + ((size_t)b * Hq + h0 + j) * D + 8 * c);
+        qv[j][0] = x.x; qv[j][1] = x.y; qv[j][2] = x.z; qv[j][3] = x.w;
+    }
+
+    float m_run[GH], l_run[GH], o[GH][8];
+#pragma unroll
+    for (int j = 0; j < GH; ++j) {
+        m_run[j] = -INFINITY;
+        l_run[j] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+    }
+
+    const size_t head_stride = (size_t)ps * D;            // one (page, head) tile
+    const size_t page_stride = (size_t)Hkv * head_stride;
+
+    uint4 kx[4], vx[4];
+    auto load_block = [&](int blk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t0 = blk * TB + i * TPI;           // first token of this load
+            if (t0 < len) {
+                const int page = __builtin_amdgcn_readfirstlane(tab[t0 >> ps_log2]);
+                const int slot = (t0 & (ps - 1)) + r;
+                const size_t off = (size_t)page * page_stride + (size_t)g * head_stride + (size_t)slot * D + 8 * c;
+                kx[i] = ld16(Kp + off);
+                vx[i] = ld16(Vp + off);
+            } else {
+                kx[i] = make_uint4(0, 0, 0, 0);
+                vx[i] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+
+    int blk = blk_begin + wave;
+    if (blk < blk_end) load_block(blk);
+    while (blk < blk_end) {
+        uint4 kc[4], vc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { kc[i] = kx[i]; vc[i] = vx[i]; }
+        const int next = blk + kWaves;
+        if (next < blk_end) load_block(next);
+
+        // logits of the lane's 4 tokens for every packed head
+        float s[4][GH];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < GH; ++j) {
+                float a = dot2(qv[j][0], kc[i].x, 0.f);
+                a = dot2(qv[j][1], kc[i].y, a);
+                a = dot2(qv[j][2], kc[i].z, a);
+                a = dot2(qv[j][3], kc[i].w, a);
+                s[i][j] = token_sum<CPT>(a);
+            }
+
+        // the block that holds the last token: drop tokens >= len
+        if ((blk + 1) * TB > len) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = blk * TB + i * TPI + r < len;
+                if (!ok) {
+#pragma unroll
+                    for (int j = 0; j < GH; ++j) s[i][j] = -INFINITY;
+                    vc[i] = make_uint4(0, 0, 0, 0);
+                }
+            }
+        }
+
+        // online softmax of this lane row, and P·V with bf16 token pairs
+        uint32_t vlo01[4], vhi01[4], vlo23[4], vhi23[4];
+        const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vc[0]);
+        const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vc[1]);
+        const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&vc[2]);
+        const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&vc[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            vlo01[e] = (v0[e] & 0xFFFFu) | (v1[e] << 16);
+            vhi01[e] = (v0[e] >> 16) | (v1[e] & 0xFFFF0000u);
+            vlo23[e] = (v2[e] & 0xFFFFu) | (v3[e] << 16);
+            vhi23[e] = (v2[e] >> 16) | (v3[e] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int j = 0; j < GH; ++j) {
+            float t[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t[i] = (s[i][j] == -INFINITY) ? -INFINITY : s[i][j] * c2;
+            const float mb = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
+            const float m_new = fmaxf(m_run[j], mb);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = exp2f(m_run[j] - m_use);
+            m_run[j] = m_new;
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(t[i] - m_use);
+            l_run[j] = l_run[j] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+            const uint32_t p01 = pack_bf16(p[0], p[1]);
+            const uint32_t p23 = pack_bf16(p[2], p[3]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o[j][2 * e] = dot2(p23, vlo23[e], dot2(p01, vlo01[e], o[j][2 * e] * alpha));
+                o[j][2 * e + 1] = dot2(p23, vhi23[e], dot2(p01, vhi01[e], o[j][2 * e + 1] * alpha));
+            }
+        }
+        blk = next;
+    }
+
+    // merge the lane rows of the wave (rows differ in lane bits >= log2(CPT))
+#pragma unroll
+    for (int j = 0; j < GH; ++j) {
+        float M = m_run[j];
+#pragma unroll
+        for (int x = CPT; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
+        const float M_use = (M == -INFINITY) ? 0.f : M;
+        const float sc = exp2f(m_run[j] - M_use);
+        float L = l_run[j] * sc;
+#pragma unroll
+        for (int x = CPT; x < 64; x <<= 1) L += __shfl_xor(L, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = o[j][e] * sc;
+#pragma unroll
+            for (int x = CPT; x < 64; x <<= 1) v += __shfl_xor(v, x);
+            o[j][e] = v;
+        }
+        if (r == 0) {
+            *reinterpret_cast<float4*>(&sh_o[wave][j][8 * c]) = make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
+            *reinterpret_cast<float4*>(&sh_o[wave][j][8 * c + 4]) = make_float4(o[j][4], o[j][5], o[j][6], o[j][7]);
+        }
+        if (lane == 0) {
+            sh_m[wave][j] = M;
+            sh_l[wave][j] = L;
+        }
+    }
+    __syncthreads();
+
+    // merge the waves and write this split's partial (m, l, o) per head
+    for (int idx = tid; idx < GH * D; idx += kThreads) {
+        const int j = idx / D, d = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sh_m[w][j]);
+        const float M_use = (M == -INFINITY) ? 0.f : M;
+        float L = 0.f, acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float sc = exp2f(sh_m[w][j] - M_use);
+            L += sh_l[w][j] * sc;
+            acc += sh_o[w][j][d] * sc;
+        }
+        const size_t unit = ((size_t)b * Hq + h0 + j) * nsplit + split;
+        ws[unit * D + d] = acc;
+        if (d == 0) {
+            float* ml = ws + (size_t)gridDim.z * Hq * nsplit * D;
+            ml[2 * unit] = M;
+            ml[2 * unit + 1] = L;
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(D)
+void decode_merge_kernel(const float* __restrict__ ws, uint16_t* __restrict__ Op, int B, int Hq, int nsplit) {
+    const int bh = blockIdx.x;
+    const int d = threadIdx.x;
+    const float* ml = ws + (size_t)B * Hq * nsplit * D;
+    const size_t u0 = (size_t)bh * nsplit;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[2 * (u0 + s)]);
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    float L = 0.f, acc = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+        const float sc = exp2f(ml[2 * (u0 + s)] - M_use);
+        L += ml[2 * (u0 + s) + 1] * sc;
+        acc += ws[(u0 + s) * D + d] * sc;
+    }
+    const float out = acc / L;
+    const __bf16 ob = (__bf16)out;
+    Op[(size_t)bh * D + d] = __builtin_bit_cast(uint16_t, ob);
+}
+
+int heads_per_group(int G) {
+    if (G <= 8) return G;
+    if (G % 8 == 0) return 8;
+    if (G % 4 == 0) return 4;
+    if (G % 2 == 0) return 2;
+    return 1;
+}
+
+template <int D, int GH>
+void launch_split(const DecodeArgs& a, int ps_log2, float c2, hipStream_t stream) {
+    const int groups = a.Hkv * ((a.Hq / a.Hkv) / GH);
+    hipLaunchKernelGGL((decode_split_kernel<D, GH>), dim3(a.nsplit, groups, a.B), dim3(kThreads), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k_pool, (const uint16_t*)a.v_pool,
+                       a.page_table, a.seq_lens, a.ws, a.Hq, a.Hkv, ps_log2, a.nsplit, c2);
+}
+
+template <int D>
+void launch_split_d(const DecodeArgs& a, int GH, int ps_log2, float c2, hipStream_t stream) {
+    switch (GH) {
+        case 8: launch_split<D, 8>(a, ps_log2, c2, stream); break;
+        case 7: launch_split<D, 7>(a, ps_log2, c2, stream); break;
+        case 6: launch_split<D, 6>(a, ps_log2, c2, stream); break;
+        case 5: launch_split<D, 5>(a, ps_log2, c2, stream); break;
+        case 4: launch_split<D, 4>(a, ps_log2, c2, stream); break;
+        case 3: launch_split<D, 3>(a, ps_log2, c2, stream); break;
+        case 2: launch_split<D, 2>(a, ps_log2, c2, stream); break;
+        default: launch_split<D, 1>(a, ps_log2, c2, stream); break;
+    }
+}
+
+}  // namespace
+
+int decode_nsplit(int B, int Hq, int Hkv, int num_cu) {
+    const int G = Hq / Hkv;
+    const long long units = (long long)B * Hkv * (G / heads_per_group(G));
+    const long long target = 16LL * (num_cu > 0 ? num_cu : 256);
+    long long n = (target + units - 1) / units;
+    if (n < 1) n = 1;
+    if (n > 64) n = 64;
+    return (int)n;
+}
+
+size_t decode_workspace_floats(int B, int Hq, int D, int nsplit) {
+    return (size_t)B * Hq * nsplit * (size_t)(D + 2);
+}
+
+hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream) {
+    int ps_log2 = 0;
+    while ((1 << ps_log2) < a.page_size) ++ps_log2;
+    const float c2 = a.scale * 1.4426950408889634f;
+    const int GH = heads_per_group(a.Hq / a.Hkv);
+    if (a.D == 128) launch_split_d<128>(a, GH, ps_log2, c2, stream);
+    else launch_split_d<64>(a, GH, ps_log2, c2, stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.D == 128)
+        hipLaunchKernelGGL((decode_merge_kernel<128>), dim3(a.B * a.Hq), dim3(128), 0, stream,
+                           (const float*)a.ws, (uint16_t*)a.o, a.B, a.Hq, a.nsplit);
+    else
+        hipLaunchKernelGGL((decode_merge_kernel<64>), dim3(a.B * a.Hq), dim3(64), 0, stream,
+                           (const float*)a.ws, (uint16_t*)a.o, a.B, a.Hq, a.nsplit);
+    return hipGetLastError();
+}
+
+}  // namespace attn

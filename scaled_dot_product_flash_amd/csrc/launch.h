@@ -1,0 +1,43 @@
+// Internal interface between the C ABI (api.cpp) and the kernel files.
+// Arguments arrive here already validated; nothing in this header is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace attn {
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    int B, Hq, Hkv, Sq, Sk, D;
+    float scale;
+    int causal, window;
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k_pool;
+    const void* v_pool;
+    const int32_t* page_table;
+    const int32_t* seq_lens;
+    void* o;
+    int B, Hq, Hkv, D, page_size;
+    float scale;
+    int nsplit;     // context splits per (sequence, head group)
+    float* ws;      // partial results, decode_workspace_floats() floats
+};
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
+
+// Number of context splits for a decode call on a device with `num_cu`
+// compute units, and the workspace (in floats) those splits need.
+int decode_nsplit(int B, int Hq, int Hkv, int num_cu);
+size_t decode_workspace_floats(int B, int Hq, int D, int nsplit);
+hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace attn

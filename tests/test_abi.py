@@ -1,0 +1,145 @@
+"""The C ABI on the host: exported symbols and argument validation.
+
+Validation runs before any HIP call, so every error path is exercised here
+without a GPU. No call in this file reaches a kernel launch: each one either
+fails validation or is an empty call.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import scaled_dot_product_flash_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, NULL, SHAPE, HEADS, HEADDIM, MASK, SCALE, PAGE, ALIGN, NOMEM, HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def _codes():
+    text = open(HEADER).read()
+    return dict((n, int(v)) for n, v in re.findall(r"\b(ATTN_\w+)\s*=\s*(-?\d+)", text))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(attn.library_path()):
+        pytest.skip("libattn.so not built")
+    return attn.load_library()
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == ["attn_decode_paged", "attn_fwd", "attn_fwd_f32", "attn_release", "attn_strerror"]
+    assert _codes() == {"ATTN_OK": OK, "ATTN_ERR_NULL": NULL, "ATTN_ERR_SHAPE": SHAPE, "ATTN_ERR_HEADS": HEADS,
+                        "ATTN_ERR_HEADDIM": HEADDIM, "ATTN_ERR_MASK": MASK, "ATTN_ERR_SCALE": SCALE,
+                        "ATTN_ERR_PAGE": PAGE, "ATTN_ERR_ALIGN": ALIGN, "ATTN_ERR_NOMEM": NOMEM, "ATTN_ERR_HIP": HIP}
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", attn.library_path()], capture_output=True, text=True).stdout
+    exported = sorted(set(re.findall(r"\bT (attn_\w+)$", out, flags=re.M)))
+    assert exported == _declared()
+
+
+def test_library_has_gfx950_code(lib):
+    out = subprocess.run(["strings", attn.library_path()], capture_output=True, text=True).stdout
+    assert "gfx950" in out
+
+
+def test_strerror_covers_every_code(lib):
+    msgs = set()
+    for name, code in _codes().items():
+        msg = attn.strerror(code)
+        assert msg and "unknown" not in msg, name
+        msgs.add(msg)
+    assert len(msgs) == len(_codes())
+    assert "unknown" in attn.strerror(12345)
+
+
+A = 4096  # a 16-byte aligned, never dereferenced address
+U = 4098  # a misaligned one
+
+
+def _fwd(lib, q=A, k=A, v=A, o=A, B=1, Hq=4, Hkv=2, Sq=8, Sk=8, D=64, scale=0.125, causal=1, window=0,
+         f32=False):
+    fn = lib.attn_fwd_f32 if f32 else lib.attn_fwd
+    return fn(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, None)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(o=None), NULL),
+    (dict(B=-1), SHAPE), (dict(Sq=-3), SHAPE), (dict(Sk=0), SHAPE), (dict(Sq=9, Sk=8), SHAPE),
+    (dict(Hq=0), HEADS), (dict(Hkv=0), HEADS), (dict(Hq=6, Hkv=4), HEADS),
+    (dict(D=96), HEADDIM), (dict(D=256), HEADDIM), (dict(D=0), HEADDIM),
+    (dict(causal=2), MASK), (dict(window=-1), MASK), (dict(causal=0, window=4), MASK),
+    (dict(scale=float("nan")), SCALE), (dict(scale=float("inf")), SCALE), (dict(scale=-float("inf")), SCALE),
+    (dict(q=U), ALIGN), (dict(k=U), ALIGN), (dict(v=U), ALIGN), (dict(o=U), ALIGN),
+    (dict(B=1 << 30, Hq=1 << 20, Hkv=1, Sq=1 << 20, Sk=1 << 20), SHAPE),
+])
+def test_prefill_validation(lib, kwargs, code, f32):
+    assert _fwd(lib, f32=f32, **kwargs) == code
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_prefill_empty_calls_are_no_ops(lib, f32):
+    # nothing to compute: no pointer is needed and no HIP call is made
+    assert _fwd(lib, q=None, k=None, v=None, o=None, B=0, f32=f32) == OK
+    assert _fwd(lib, q=None, k=None, v=None, o=None, Sq=0, f32=f32) == OK
+    assert _fwd(lib, q=None, k=None, v=None, o=None, Sq=0, causal=0, f32=f32) == OK
+
+
+def _dec(lib, q=A, kp=A, vp=A, pt=A, sl=A, o=A, B=2, Hq=8, Hkv=2, D=128, ps=16, scale=0.1):
+    return lib.attn_decode_paged(q, kp, vp, pt, sl, B, Hq, Hkv, D, ps, scale, o, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(q=None), NULL), (dict(kp=None), NULL), (dict(vp=None), NULL), (dict(pt=None), NULL),
+    (dict(sl=None), NULL), (dict(o=None), NULL),
+    (dict(B=-1), SHAPE), (dict(B=70000), SHAPE),
+    (dict(Hq=0), HEADS), (dict(Hkv=0), HEADS), (dict(Hq=8, Hkv=3), HEADS),
+    (dict(D=32), HEADDIM),
+    (dict(ps=0), PAGE), (dict(ps=4), PAGE), (dict(ps=12), PAGE), (dict(ps=512), PAGE), (dict(ps=-16), PAGE),
+    (dict(scale=float("nan")), SCALE),
+    (dict(q=U), ALIGN), (dict(kp=U), ALIGN), (dict(vp=U), ALIGN), (dict(o=U), ALIGN), (dict(pt=A + 2), ALIGN),
+    (dict(sl=A + 1), ALIGN),
+])
+def test_decode_validation(lib, kwargs, code):
+    assert _dec(lib, **kwargs) == code
+
+
+def test_decode_empty_batch_is_a_no_op(lib):
+    assert _dec(lib, q=None, kp=None, vp=None, pt=None, sl=None, o=None, B=0) == OK
+
+
+def test_release_without_work_is_a_no_op(lib):
+    lib.attn_release()
+    lib.attn_release()
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    import torch
+
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attn.fwd(q, q, q)
+    with pytest.raises(ValueError):
+        attn.decode_paged(q[0], q, q, torch.zeros(1, dtype=torch.int32), torch.ones(1, dtype=torch.int32))
+
+
+def test_ctypes_signature_matches_header(lib):
+    assert lib.attn_fwd.restype is ctypes.c_int
+    assert len(lib.attn_fwd.argtypes) == 14
+    assert len(lib.attn_decode_paged.argtypes) == 13

@@ -1,0 +1,147 @@
+"""GPU parity of attn_decode_paged against the float64 oracle.
+
+Padding slots of every sequence's last page hold NaN, so any read of a token
+at or past seq_lens[b] shows up as a non-finite output.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scaled_dot_product_flash_amd as attn
+from scaled_dot_product_flash_amd import inputs
+from gpu_util import check_bf16, cuda, f64, needs_gpu, say
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def _run(d, scale):
+    q, kp, vp, pt, sl = cuda(d["q"], d["k_pool"], d["v_pool"], d["page_table"], d["seq_lens"])
+    o = attn.decode_paged(q, kp, vp, pt, sl, scale=scale)
+    torch.cuda.synchronize()
+    return o.cpu()
+
+
+def _oracle(d, scale):
+    return oracle.decode_paged(f64(d["q"]), d["k_pool"].float().numpy(), d["v_pool"].float().numpy(),
+                               d["page_table"].numpy(), d["seq_lens"].numpy(), d["k_pool"].shape[2], scale)
+
+
+def test_paged_decode_workload():
+    w = inputs.WORKLOADS["paged_decode"]
+    say("decode workload paged_decode")
+    d = inputs.workload_inputs("paged_decode")
+    scale = 1.0 / math.sqrt(w["D"])
+    got = _run(d, scale)
+    check_bf16(f64(got), _oracle(d, scale), "paged_decode")
+
+
+CASES = [
+    # nseq, Hq, Hkv, D, page_size, seq_lens
+    (1, 1, 1, 128, 16, [1]),
+    (3, 4, 4, 64, 8, [1, 8, 9]),
+    (4, 8, 2, 128, 16, [15, 16, 17, 33]),
+    (5, 32, 8, 128, 16, [500, 1, 64, 63, 1000]),
+    (2, 16, 1, 128, 32, [700, 5]),          # MQA, 16 heads per K/V head
+    (3, 12, 12, 64, 64, [130, 64, 1]),
+    (2, 8, 2, 128, 256, [300, 1000]),
+    (2, 6, 2, 64, 128, [129, 2]),           # 3 heads per K/V head
+    (64, 4, 2, 128, 16, list(range(1, 65))),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_decode_cases(case):
+    nseq, Hq, Hkv, D, ps, lens = case
+    say(f"decode nseq={nseq} Hq={Hq} Hkv={Hkv} D={D} ps={ps}")
+    d = inputs.decode_inputs(nseq, Hq, Hkv, D, ps, 0, 0, "bf16", seed=nseq + Hq + D + ps, seq_lens=lens)
+    scale = 1.0 / math.sqrt(D)
+    check_bf16(f64(_run(d, scale)), _oracle(d, scale), str(case))
+
+
+def test_many_short_sequences():
+    d = inputs.decode_inputs(2000, 8, 2, 128, 16, 1, 40, "bf16", seed=31)
+    scale = 0.1
+    check_bf16(f64(_run(d, scale)), _oracle(d, scale), "2000 short sequences")
+
+
+def test_permuted_pages_equal_identity_bit_exact():
+    lens = [900, 17, 4000, 256]
+    a = inputs.decode_inputs(4, 16, 4, 128, 16, 0, 0, "bf16", seed=32, seq_lens=lens, permute=False)
+    b = inputs.decode_inputs(4, 16, 4, 128, 16, 0, 0, "bf16", seed=32, seq_lens=lens, permute=True)
+    # same token values, scattered through the pool by the page table
+    counts = [(n + 15) // 16 for n in lens]
+    assert b["k_pool"].shape[0] == sum(counts)
+    for name in ("k_pool", "v_pool"):
+        src = a[name]
+        dst = torch.empty_like(src)
+        dst[b["page_table"].long()] = src[torch.arange(src.shape[0])]
+        b[name] = dst
+    b["q"] = a["q"]
+    assert torch.equal(_run(a, 0.09), _run(b, 0.09))
+
+
+def test_decode_equals_last_prefill_row():
+    # one decode step over a cache of t tokens is row t-1 of a causal prefill
+    # ("拆开 LLM（二）", KV-cache section: cached and full recomputation agree)
+    S, Hq, Hkv, D, ps = 300, 8, 2, 128, 16
+    q, k, v = inputs.prefill_inputs(1, Hq, Hkv, S, S, D, "bf16", 33)
+    scale = 1.0 / math.sqrt(D)
+    full = attn.fwd(*cuda(q, k, v), scale=scale, causal=True).cpu()
+    for t in (1, 16, 17, 150, 300):
+        n_pages = (t + ps - 1) // ps
+        kp = torch.zeros(n_pages * ps, Hkv, D, dtype=torch.bfloat16)
+        vp = torch.zeros_like(kp)
+        kp[:t] = k[0, :, :t].transpose(0, 1)
+        vp[:t] = v[0, :, :t].transpose(0, 1)
+        kp = kp.view(n_pages, ps, Hkv, D).transpose(1, 2).contiguous()
+        vp = vp.view(n_pages, ps, Hkv, D).transpose(1, 2).contiguous()
+        d = dict(q=q[0, :, t - 1][None].contiguous(), k_pool=kp, v_pool=vp,
+                 page_table=torch.arange(n_pages, dtype=torch.int32), seq_lens=torch.tensor([t], dtype=torch.int32))
+        step = _run(d, scale)
+        check_bf16(f64(step[0]), f64(full[0, :, t - 1]), f"t={t}")
+        check_bf16(f64(step), _oracle(d, scale), f"t={t} vs oracle")
+
+
+def test_paged_position_probe():
+    # Q = 0: uniform weights; V slot of logical token t holds the bits of t
+    lens, ps, D = [3, 16, 33, 1000], 16, 64
+    d = inputs.decode_inputs(len(lens), 4, 2, D, ps, 0, 0, "bf16", seed=34, seq_lens=lens, nan_pad=True)
+    d["q"] = torch.zeros_like(d["q"])
+    first = 0
+    for n in lens:
+        c = (n + ps - 1) // ps
+        for p in range(c):
+            page = int(d["page_table"][first + p])
+            for s in range(ps):
+                t = p * ps + s
+                if t < n:
+                    bits = ((t >> torch.arange(D)) & 1).to(torch.bfloat16)
+                    d["v_pool"][page, :, s] = bits
+        first += c
+    got = f64(_run(d, 1.0))
+    for b, n in enumerate(lens):
+        ts = np.arange(n)
+        want = ((ts[:, None] >> np.arange(D)[None, :]) & 1).mean(0)
+        rel = np.abs(got[b] - want[None]) / np.maximum(want[None], 1e-30)
+        assert rel.max() <= 2 ** -8, (b, rel.max())
+
+
+def test_repeated_calls_and_streams_agree():
+    d = inputs.decode_inputs(8, 8, 2, 128, 16, 10, 900, "bf16", seed=35)
+    first = _run(d, 0.1)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        q, kp, vp, pt, sl = cuda(d["q"], d["k_pool"], d["v_pool"], d["page_table"], d["seq_lens"])
+        o = attn.decode_paged(q, kp, vp, pt, sl, scale=0.1)
+    s.synchronize()
+    assert torch.equal(o.cpu(), first)
+    # a larger call grows the workspace; a smaller one after it reuses it
+    big = inputs.decode_inputs(200, 32, 8, 128, 16, 10, 300, "bf16", seed=36)
+    check_bf16(f64(_run(big, 0.1)), _oracle(big, 0.1), "grown workspace")
+    assert torch.equal(_run(d, 0.1), first)
+    attn.release()
+    assert torch.equal(_run(d, 0.1), first)
