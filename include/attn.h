@@ -41,8 +41,10 @@ enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = -1,     /* a required pointer is NULL */
     ATTN_ERR_SHAPE = -2,    /* a size is negative or zero where it must be >= 1,
-                               causal with Sq > Sk, or an element count
-                               overflows 64-bit addressing */
+                               causal with Sq > Sk, an element count overflows
+                               64-bit addressing, or one (batch, kv head) slice
+                               of K/V exceeds 2^31 bytes in float32
+                               (Sk * D * 4 >= 2^31) */
     ATTN_ERR_HEADS = -3,    /* Hq < 1, Hkv < 1 or Hq % Hkv != 0 */
     ATTN_ERR_HEADDIM = -4,  /* D is not 64 or 128 */
     ATTN_ERR_MASK = -5,     /* causal not 0/1, window < 0, or window > 0 without causal */

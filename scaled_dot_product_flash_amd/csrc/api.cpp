@@ -38,6 +38,8 @@ int validate_prefill(const void* q, const void* k, const void* v, const void* o,
     if (Sk < 1) return ATTN_ERR_SHAPE;
     if (causal && Sq > Sk) return ATTN_ERR_SHAPE;
     if (!product_fits(B, Hq, Sq, D) || !product_fits(B, Hkv, Sk, D)) return ATTN_ERR_SHAPE;
+    // one (batch, kv head) slice of K or V is addressed with 32-bit byte offsets
+    if ((long long)Sk * D * 4 > 0x7FFFFFFFLL) return ATTN_ERR_SHAPE;
     // grid of either kernel (at most one workgroup per 64 rows, rounded to 8)
     const long long items = (long long)B * Hq * ((Sq + 63) / 64) + 8;
     if (items > 0x7FFFFFFFLL) return ATTN_ERR_SHAPE;

@@ -44,6 +44,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -60,11 +64,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
-// Position of key kappa (within a tile) in the transposed V tile: bits 2 and
-// 3 swapped, so the 8 keys a lane contributes to one P^T·V MFMA k-step are
-// adjacent and one 16-byte LDS read fetches them.
-__device__ __forceinline__ int vt_pos(int kappa) {
-    return (kappa & ~0xC) | ((kappa & 4) << 1) | ((kappa & 8) >> 1);
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format).
+constexpr int kRsrcWord3 = 0x00020000;
+// Lazy-rescale threshold for the reference maximum, log2 units.
+constexpr float kLazy = 8.0f;
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
 template <int D, bool NEG>
@@ -78,15 +84,16 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     constexpr int KS = BN / 16;           // 16-key MFMA k-steps per tile (P·V)
     constexpr int DS = D / 16;            // 16-wide d steps (Q·K^T)
     constexpr int DB = D / 32;            // 32-row d blocks of O^T
-    constexpr int CPR = D / 8;            // 16-byte chunks per K row
-    constexpr int K_BYTES = BN * D * 2;
-    constexpr int V_BYTES = D * BN * 2;
-    constexpr int BUF_BYTES = K_BYTES + V_BYTES;
-    constexpr int KCH = BN * D / 8 / kThreads;  // K chunks per thread per tile
-    static_assert(KCH * kThreads * 8 == BN * D, "K tile split");
-    static_assert((BN / 4) * (D / 8) == kThreads, "V tile split");
+    constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
+    constexpr int TILE_BYTES = BN * D * 2;
+    constexpr int SLOTS = TILE_BYTES / 1024;    // 1 KiB DMA slots per tile and tensor
+    static_assert(SLOTS % kWaves == 0, "DMA slots per wave");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF_BYTES];
+    // two pipeline stages, each its own LDS object
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds1[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds1[TILE_BYTES];
 
     // ---- work item -------------------------------------------------------
     const int w = blockIdx.x;
@@ -102,7 +109,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     const int h = g * G + hg;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int ln = lane & 31;
     const int hh = lane >> 5;
@@ -113,8 +120,11 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
 
     const size_t qo_base = ((size_t)b * Hq + h) * (size_t)Sq * D;
     const size_t kv_base = ((size_t)b * Hkv + g) * (size_t)Sk * D;
-    const uint16_t* Kb = K + kv_base;
-    const uint16_t* Vb = V + kv_base;
+    // Buffer resources over this (batch, kv head) slice: rows past Sk read
+    // as zeros instead of outside the slice.
+    const int kv_bytes = Sk * D * 2;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(K + kv_base), 0, kv_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(V + kv_base), 0, kv_bytes, kRsrcWord3);
 
     // key range of the whole workgroup
     const int p_first = i0 + off;
@@ -148,55 +158,24 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         }
     }
 
-    // ---- tile staging -----------------------------------------------------
-    uint4 kreg[KCH];
-    uint4 vreg[4];
-    const int vm = tid % (BN / 4);   // V task: keys 4*vm .. 4*vm+3
-    const int vc = tid / (BN / 4);   //         d   8*vc .. 8*vc+7
-
-    auto load_tile = [&](int t) {
+    // ---- tile staging: buffer -> LDS DMA, 1 KiB per wave instruction --------
+    // K rows keep their 16-byte chunks XOR-swizzled by kswz(row) and V rows by
+    // vswz(row); the DMA realises the swizzle through the per-lane source
+    // offset because its LDS destination is always base + 16 * lane.
+    auto kswz = [](int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
+    auto vswz = [](int row) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); };
+    auto issue_tile = [&](int t, unsigned char* kdst, unsigned char* vdst) {
         const int j0 = t * BN;
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int id = i * kThreads + tid;
-            const int key = id / CPR, cc = id % CPR;
-            const int j = j0 + key;
-            kreg[i] = (j < Sk) ? ld_global16(Kb + (size_t)j * D + 8 * cc) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
-            const int j = j0 + 4 * vm + t4;
-            vreg[t4] = (j < Sk) ? ld_global16(Vb + (size_t)j * D + 8 * vc) : make_uint4(0, 0, 0, 0);
-        }
-    };
-
-    auto store_tile = [&](int buf) {
-        unsigned char* kb = smem + buf * BUF_BYTES;
-        unsigned char* vb = kb + K_BYTES;
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int id = i * kThreads + tid;
-            const int key = id / CPR, cc = id % CPR;
-            *reinterpret_cast<uint4*>(kb + key * (D * 2) + ((cc ^ (key & 7)) << 4)) = kreg[i];
-        }
-        const int pos = vt_pos(4 * vm);
-        const int chunk = pos >> 3;
-        const int half8 = (pos & 7) * 2;  // 0 or 8 bytes into the chunk
-        const uint32_t* x0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
-        const uint32_t* x1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
-        const uint32_t* x2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
-        const uint32_t* x3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int d0 = 8 * vc + 2 * e;
-            const int d1 = d0 + 1;
-            uint2 lo, hi2;
-            lo.x = (x0[e] & 0xFFFFu) | (x1[e] << 16);
-            lo.y = (x2[e] & 0xFFFFu) | (x3[e] << 16);
-            hi2.x = (x0[e] >> 16) | (x1[e] & 0xFFFF0000u);
-            hi2.y = (x2[e] >> 16) | (x3[e] & 0xFFFF0000u);
-            *reinterpret_cast<uint2*>(vb + d0 * (BN * 2) + ((chunk ^ (d0 & 7)) << 4) + half8) = lo;
-            *reinterpret_cast<uint2*>(vb + d1 * (BN * 2) + ((chunk ^ (d1 & 7)) << 4) + half8) = hi2;
+        for (int i = 0; i < SLOTS / kWaves; ++i) {
+            const int sl = wave + kWaves * i;
+            const int u = sl * 64 + lane;          // 16-byte unit of the tile
+            const int row = u / CPR, phys = u % CPR;
+            const int kc = phys ^ kswz(row), vcn = phys ^ vswz(row);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + sl * 1024), 16,
+                                                     ((j0 + row) * D + 8 * kc) * 2, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + sl * 1024), 16,
+                                                     ((j0 + row) * D + 8 * vcn) * 2, 0, 0, 0);
         }
     };
 
@@ -206,119 +185,153 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
-    float m_run = -INFINITY;  // running max of scaled logits, log2 units
-    float l_run = 0.f;        // this lane's share of the running row sum
+    // Reference maximum of the scaled logits (log2 units). It only moves when
+    // a tile's maximum exceeds it by more than kLazy, so most tiles skip the
+    // rescale of O; probabilities stay <= 2^kLazy, and because numerator and
+    // denominator share the same reference the result is unchanged.
+    float m_run = -INFINITY;
+    float l_run = 0.f;        // this lane's share of the row sum (of bf16 P)
+    const uint32_t ones = 0x3F803F80u;  // bf16 pair (1, 1)
 
-    load_tile(t_begin);
-    store_tile(0);
-    __syncthreads();
+    // V^T operand reads: a 16-lane group reads 4 keys x 16 d with the
+    // transposing LDS read, lane i of the group receiving d = base + i.
+    const int grp = (lane >> 4) & 1;         // which 16 d of the 32-d block
+    const int e4 = (lane & 15) >> 2;         // key offset within the 4 keys
+    const int q4 = lane & 3;                 // 4-d column group
+    auto vread = [&](const unsigned char* vb, int key, int d) -> s16x4 {
+        const int off_b = key * (D * 2) + (((d >> 3) ^ vswz(key)) << 4) + ((d & 7) << 1);
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + off_b));
+    };
 
-    for (int t = t_begin; t < t_end; ++t) {
-        const int cur = (t - t_begin) & 1;
-        const bool has_next = t + 1 < t_end;
-        if (has_next) load_tile(t + 1);
-        const int j0 = t * BN;
-        const bool active = wave_rows && j0 <= w_hi && j0 + BN - 1 >= w_lo;
-        if (active) {
-            const unsigned char* kb = smem + cur * BUF_BYTES;
-            const unsigned char* vb = kb + K_BYTES;
-
-            // S^T = K_tile · Q^T, 32 keys x 32 queries per accumulator
-            f32x16 sacc[KB];
+    // One K/V tile: S^T = K·Q^T, online softmax, O^T += V^T·P^T. `edge` tiles
+    // straddle a mask boundary or the key tail; only they evaluate the mask,
+    // in two wave-uniform branches the other tiles jump over.
+    auto tile = [&](const unsigned char* kb, const unsigned char* vb, int j0, bool edge) {
+        f32x16 sacc[KB];
 #pragma unroll
-            for (int kbk = 0; kbk < KB; ++kbk)
+        for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) sacc[kbk][v] = 0.f;
+            for (int v = 0; v < 16; ++v) sacc[kbk][v] = 0.f;
 #pragma unroll
-            for (int s = 0; s < DS; ++s) {
+        for (int s = 0; s < DS; ++s) {
 #pragma unroll
-                for (int kbk = 0; kbk < KB; ++kbk) {
-                    const int key = 32 * kbk + ln;
-                    const int cc = 2 * s + hh;
-                    const uint4 a = *reinterpret_cast<const uint4*>(kb + key * (D * 2) + ((cc ^ (key & 7)) << 4));
-                    sacc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qreg[s], sacc[kbk], 0, 0, 0);
-                }
+            for (int kbk = 0; kbk < KB; ++kbk) {
+                const int key = 32 * kbk + ln;
+                const int cc = 2 * s + hh;
+                const uint4 a = *reinterpret_cast<const uint4*>(kb + key * (D * 2) + ((cc ^ kswz(key)) << 4));
+                sacc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qreg[s], sacc[kbk], 0, 0, 0);
             }
+        }
 
-            // mask (boundary tiles only) and the tile's extreme raw logit
-            const bool edge = (j0 + BN - 1 > w_full_hi) || (j0 < w_full_lo);
-            const float masked = NEG ? INFINITY : -INFINITY;
-            uint64_t vis = ~0ull;
-            float mx = masked;
-            if (edge) {
-                vis = 0;
-#pragma unroll
-                for (int kbk = 0; kbk < KB; ++kbk)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int j = j0 + 32 * kbk + 8 * (v >> 2) + 4 * hh + (v & 3);
-                        bool ok = j < Sk;
-                        if (causal) ok = ok && j <= qpos;
-                        if (window > 0) ok = ok && j > qpos - window;
-                        vis |= (uint64_t)ok << (16 * kbk + v);
-                        const float x = ok ? sacc[kbk][v] : masked;
-                        mx = NEG ? fminf(mx, x) : fmaxf(mx, x);
-                    }
-            } else {
-#pragma unroll
-                for (int kbk = 0; kbk < KB; ++kbk)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        mx = NEG ? fminf(mx, sacc[kbk][v]) : fmaxf(mx, sacc[kbk][v]);
-            }
-            const float other = xor32(mx);
-            mx = NEG ? fminf(mx, other) : fmaxf(mx, other);
-
-            // online softmax update (log2 domain: exp(x) = exp2(x * log2 e))
-            const float mt = (mx == masked) ? -INFINITY : mx * c2;
-            const float m_new = fmaxf(m_run, mt);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = exp2f(m_run - m_use);
-            m_run = m_new;
-
-            float lsum = 0.f;
+        // tile extreme of the raw logits (max, or min for a negative scale)
+        const float masked = NEG ? INFINITY : -INFINITY;
+        uint64_t vis = ~0ull;
+        float mx = masked;
+        if (edge) {
+            vis = 0;
 #pragma unroll
             for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    float p = __builtin_amdgcn_exp2f(fmaf(sacc[kbk][v], c2, -m_use));
-                    if (edge) p = ((vis >> (16 * kbk + v)) & 1) ? p : 0.f;
-                    sacc[kbk][v] = p;
-                    lsum += p;
+                    const int j = j0 + 32 * kbk + 8 * (v >> 2) + 4 * hh + (v & 3);
+                    bool ok = j < Sk;
+                    if (causal) ok = ok && j <= qpos;
+                    if (window > 0) ok = ok && j > qpos - window;
+                    vis |= (uint64_t)ok << (16 * kbk + v);
+                    const float x = ok ? sacc[kbk][v] : masked;
+                    mx = NEG ? fminf(mx, x) : fmaxf(mx, x);
                 }
-            l_run = l_run * alpha + lsum;
+        } else {
+#pragma unroll
+            for (int kbk = 0; kbk < KB; ++kbk)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    mx = NEG ? fminf(mx, sacc[kbk][v]) : fmaxf(mx, sacc[kbk][v]);
+        }
+        const float other = xor32(mx);
+        mx = NEG ? fminf(mx, other) : fmaxf(mx, other);
+        const float mt = (mx == masked) ? -INFINITY : mx * c2;
+
+        // move the reference maximum only when this tile exceeds it by kLazy
+        const bool need = mt > m_run + kLazy;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            // lanes that keep their reference scale by 1 (m_run may still be
+            // -inf there, and -inf - -inf would be NaN); a first finite
+            // maximum scales by exp2(-inf) = 0, clearing nothing but zeros
+            const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
+            m_run = need ? mt : m_run;
+            l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+        }
 
-            // P^T as bf16 B operands, straight from the accumulators
-            bf16x8 pb[KS];
+        // P = exp2(s * c2 - m); masked entries are replaced by exact zeros
+        // (selection, so an overflowing masked logit never matters)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
+        for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
-                for (int j = 0; j < 8; j += 2) {
-                    f32x2 pr = {sacc[ks >> 1][8 * (ks & 1) + j], sacc[ks >> 1][8 * (ks & 1) + j + 1]};
-                    bf16x2 pbf = __builtin_convertvector(pr, bf16x2);
-                    pb[ks][j] = pbf[0];
-                    pb[ks][j + 1] = pbf[1];
-                }
-            }
+            for (int v = 0; v < 16; ++v)
+                sacc[kbk][v] = __builtin_amdgcn_exp2f(fmaf(sacc[kbk][v], c2, -m_run));
+        if (edge) {
+#pragma unroll
+            for (int kbk = 0; kbk < KB; ++kbk)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    sacc[kbk][v] = ((vis >> (16 * kbk + v)) & 1) ? sacc[kbk][v] : 0.f;
+        }
 
-            // O^T += V^T · P^T
+        // bf16 pairs of P as MFMA B operands; l += the same rounded values
+        bf16x8 pb[KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const int d = 32 * db + ln;
-                    const int q8 = 2 * ks + hh;
-                    const uint4 a = *reinterpret_cast<const uint4*>(vb + d * (BN * 2) + ((q8 ^ (d & 7)) << 4));
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pb[ks], oacc[db], 0, 0, 0);
-                }
+            for (int j = 0; j < 8; j += 2) {
+                const int kbk = ks >> 1, v0 = 8 * (ks & 1) + j;
+                f32x2 pr = {sacc[kbk][v0], sacc[kbk][v0 + 1]};
+                const bf16x2 pbf = __builtin_convertvector(pr, bf16x2);
+                l_run = __builtin_amdgcn_fdot2_f32_bf16(pbf, __builtin_bit_cast(bf16x2, ones), l_run, false);
+                pb[ks][j] = pbf[0];
+                pb[ks][j + 1] = pbf[1];
             }
         }
-        if (has_next) store_tile(cur ^ 1);
+
+        // O^T += V^T · P^T. For k-step ks (keys 16*ks .. 16*ks+15 of the tile)
+        // the accumulator hands lane-half hh the keys 16ks + 4hh + {0..3} and
+        // 16ks + 8 + 4hh + {0..3}; two transposing reads fetch exactly those.
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int key0 = 16 * ks + 4 * hh + e4;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int d = 32 * db + 16 * grp + 4 * q4;
+                const s16x4 lo4 = vread(vb, key0, d);
+                const s16x4 hi4 = vread(vb, key0 + 8, d);
+                const s16x8 a8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[ks], oacc[db], 0, 0, 0);
+            }
+        }
+    };
+
+    auto step = [&](int t, unsigned char* kcur, unsigned char* vcur, unsigned char* knext, unsigned char* vnext) {
+        if (t + 1 < t_end) issue_tile(t + 1, knext, vnext);
+        const int j0 = t * BN;
+        const bool active = wave_rows && j0 <= w_hi && j0 + BN - 1 >= w_lo;
+        if (active) {
+            const bool edge = (j0 + BN - 1 > w_full_hi) || (j0 < w_full_lo);
+            tile(kcur, vcur, j0, edge);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+    };
+
+    issue_tile(t_begin, k_lds0, v_lds0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int t = t_begin; t < t_end; t += 2) {
+        step(t, k_lds0, v_lds0, k_lds1, v_lds1);
+        if (t + 1 < t_end) step(t + 1, k_lds1, v_lds1, k_lds0, v_lds0);
     }
 
     // ---- epilogue: O = O^T / l, bf16, 4 consecutive d per 8-byte store -----

@@ -102,6 +102,8 @@ SHAPES = [
     (1, 2, 2, 130, 130, 128, True, 64),     # window of exactly one tile
     (1, 2, 1, 500, 700, 128, True, 100),    # window, Sq < Sk
     (1, 2, 2, 190, 190, 64, True, 5000),    # window wider than the sequence
+    (1, 4, 2, 100, 150, 128, True, 8),      # first tile: some rows of a wave see no key
+    (1, 2, 2, 60, 170, 64, True, 8),        # the same across a 128-key tile
     (2, 16, 4, 1000, 1000, 128, True, 0),
     (1, 4, 4, 1000, 1000, 64, True, 0),
 ]
