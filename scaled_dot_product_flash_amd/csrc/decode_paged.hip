@@ -52,21 +52,29 @@ __device__ __forceinline__ float dpp(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over the lanes that hold one token: 16 lanes (a DPP row) for D = 128,
-// 8 lanes (half a row) for D = 64. Every lane of the group gets the sum.
-template <int CPT>
-__device__ __forceinline__ float token_sum(float x) {
+// Sum over the lanes that hold one token, for N independent values at once:
+// 16 lanes (a DPP row) for D = 128, 8 lanes (half a row) for D = 64. Every
+// lane of the group ends with the sums. Each step is applied to all N values
+// before the next, so no value waits on its own previous DPP result.
+template <int CPT, int N>
+__device__ __forceinline__ void token_sum_all(float* x) {
     if constexpr (CPT == 16) {
-        x += dpp<0x128>(x);  // row_ror:8
-        x += dpp<0x124>(x);  // row_ror:4
-        x += dpp<0x122>(x);  // row_ror:2
-        x += dpp<0x121>(x);  // row_ror:1
+#pragma unroll
+        for (int n = 0; n < N; ++n) x[n] += dpp<0x128>(x[n]);  // row_ror:8
+#pragma unroll
+        for (int n = 0; n < N; ++n) x[n] += dpp<0x124>(x[n]);  // row_ror:4
+#pragma unroll
+        for (int n = 0; n < N; ++n) x[n] += dpp<0x122>(x[n]);  // row_ror:2
+#pragma unroll
+        for (int n = 0; n < N; ++n) x[n] += dpp<0x121>(x[n]);  // row_ror:1
     } else {
-        x += dpp<0x141>(x);  // row_half_mirror: lane i + lane 7-i
-        x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
-        x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+#pragma unroll
+        for (int n = 0; n < N; ++n) x[n] += dpp<0x141>(x[n]);  // row_half_mirror: lane i + lane 7-i
+#pragma unroll
+        for (int n = 0; n < N; ++n) x[n] += dpp<0xB1>(x[n]);   // quad_perm [1,0,3,2]
+#pragma unroll
+        for (int n = 0; n < N; ++n) x[n] += dpp<0x4E>(x[n]);   // quad_perm [2,3,0,1]
     }
-    return x;
 }
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -78,9 +86,20 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-template <int D, int GH>
+__device__ __forceinline__ uint4 ld16_nt(const uint16_t* p) {
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(x.x, x.y, x.z, x.w);
+}
+
+// Lazy-rescale threshold for the reference maximum, log2 units.
+constexpr float kLazy = 8.0f;
+constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
+
+template <int D, int GH, bool NEG>
 __global__ __launch_bounds__(kThreads)
 void decode_split_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __restrict__ Kp,
                          const uint16_t* __restrict__ Vp, const int32_t* __restrict__ table,
@@ -145,17 +164,20 @@ void decode_split_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __rest
     const size_t head_stride = (size_t)ps * D;            // one (page, head) tile
     const size_t page_stride = (size_t)Hkv * head_stride;
 
-    uint4 kx[4], vx[4];
-    auto load_block = [&](int blk) {
+    // K/V pages are streamed once per decode step: nontemporal loads keep them
+    // from displacing other data in the caches. The page base is wave-uniform
+    // (scalar), the lane's offset inside the (page, head) tile is 32-bit.
+    const int lane_off = r * D + 8 * c;
+    auto load_block = [&](int blk, uint4 (&kx)[4], uint4 (&vx)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t0 = blk * TB + i * TPI;           // first token of this load
             if (t0 < len) {
                 const int page = __builtin_amdgcn_readfirstlane(tab[t0 >> ps_log2]);
-                const int slot = (t0 & (ps - 1)) + r;
-                const size_t off = (size_t)page * page_stride + (size_t)g * head_stride + (size_t)slot * D + 8 * c;
-                kx[i] = ld16(Kp + off);
-                vx[i] = ld16(Vp + off);
+                const size_t tile = (size_t)page * page_stride + (size_t)g * head_stride +
+                                    (size_t)(t0 & (ps - 1)) * D;
+                kx[i] = ld16_nt(Kp + tile + lane_off);
+                vx[i] = ld16_nt(Vp + tile + lane_off);
             } else {
                 kx[i] = make_uint4(0, 0, 0, 0);
                 vx[i] = make_uint4(0, 0, 0, 0);
@@ -163,42 +185,47 @@ void decode_split_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __rest
         }
     };
 
-    int blk = blk_begin + wave;
-    if (blk < blk_end) load_block(blk);
-    while (blk < blk_end) {
-        uint4 kc[4], vc[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { kc[i] = kx[i]; vc[i] = vx[i]; }
-        const int next = blk + kWaves;
-        if (next < blk_end) load_block(next);
-
-        // logits of the lane's 4 tokens for every packed head
+    // one 16/32-token block already in registers: logits, online softmax, P·V
+    auto process = [&](int blk, const uint4 (&kc)[4], uint4 (&vc)[4]) {
+        // raw logits q.k of the lane's 4 tokens for every packed head; the
+        // 4*GH dot products and their lane sums advance in lock-step so that
+        // independent instructions sit between the dependent DPP steps
         float s[4][GH];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < GH; ++j) {
-                float a = dot2(qv[j][0], kc[i].x, 0.f);
-                a = dot2(qv[j][1], kc[i].y, a);
-                a = dot2(qv[j][2], kc[i].z, a);
-                a = dot2(qv[j][3], kc[i].w, a);
-                s[i][j] = token_sum<CPT>(a);
-            }
+            for (int j = 0; j < GH; ++j) s[i][j] = dot2(qv[j][0], kc[i].x, 0.f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < GH; ++j) s[i][j] = dot2(qv[j][1], kc[i].y, s[i][j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < GH; ++j) s[i][j] = dot2(qv[j][2], kc[i].z, s[i][j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < GH; ++j) s[i][j] = dot2(qv[j][3], kc[i].w, s[i][j]);
+        token_sum_all<CPT, 4 * GH>(&s[0][0]);
 
-        // the block that holds the last token: drop tokens >= len
-        if ((blk + 1) * TB > len) {
+        // the block holding the last token: tokens >= len get an extreme
+        // logit that never wins the max, and their V rows become zeros
+        const bool partial = (blk + 1) * TB > len;
+        bool ok[4] = {true, true, true, true};
+        if (partial) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool ok = blk * TB + i * TPI + r < len;
-                if (!ok) {
+                ok[i] = blk * TB + i * TPI + r < len;
+                if (!ok[i]) {
 #pragma unroll
-                    for (int j = 0; j < GH; ++j) s[i][j] = -INFINITY;
+                    for (int j = 0; j < GH; ++j) s[i][j] = NEG ? INFINITY : -INFINITY;
                     vc[i] = make_uint4(0, 0, 0, 0);
                 }
             }
         }
 
-        // online softmax of this lane row, and P·V with bf16 token pairs
+        // V re-paired over tokens (0,1) and (2,3) for the bf16 pair products
         uint32_t vlo01[4], vhi01[4], vlo23[4], vhi23[4];
         const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vc[0]);
         const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vc[1]);
@@ -211,28 +238,57 @@ void decode_split_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __rest
             vlo23[e] = (v2[e] & 0xFFFFu) | (v3[e] << 16);
             vhi23[e] = (v2[e] >> 16) | (v3[e] & 0xFFFF0000u);
         }
+
 #pragma unroll
         for (int j = 0; j < GH; ++j) {
-            float t[4];
+            // this lane row's extreme raw logit -> scaled maximum (log2 units)
+            const float mx = NEG ? fminf(fminf(s[0][j], s[1][j]), fminf(s[2][j], s[3][j]))
+                                 : fmaxf(fmaxf(s[0][j], s[1][j]), fmaxf(s[2][j], s[3][j]));
+            const float mt = (mx == (NEG ? INFINITY : -INFINITY)) ? -INFINITY : mx * c2;
+            // lazy reference maximum: move it only when exceeded by kLazy, so
+            // p <= 2^kLazy and o is rescaled rarely (same reference in o and l)
+            const bool need = mt > m_run[j] + kLazy;
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                const float alpha = need ? __builtin_amdgcn_exp2f(m_run[j] - mt) : 1.f;
+                m_run[j] = need ? mt : m_run[j];
+                l_run[j] *= alpha;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) t[i] = (s[i][j] == -INFINITY) ? -INFINITY : s[i][j] * c2;
-            const float mb = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
-            const float m_new = fmaxf(m_run[j], mb);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = exp2f(m_run[j] - m_use);
-            m_run[j] = m_new;
+                for (int e = 0; e < 8; ++e) o[j][e] *= alpha;
+            }
             float p[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(t[i] - m_use);
-            l_run[j] = l_run[j] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+            for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(s[i][j], c2, -m_run[j]));
+            if (partial) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p[i] = ok[i] ? p[i] : 0.f;
+            }
             const uint32_t p01 = pack_bf16(p[0], p[1]);
             const uint32_t p23 = pack_bf16(p[2], p[3]);
+            // l sums the same bf16-rounded probabilities that weight V
+            l_run[j] = dot2(p23, kOnes, dot2(p01, kOnes, l_run[j]));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                o[j][2 * e] = dot2(p23, vlo23[e], dot2(p01, vlo01[e], o[j][2 * e] * alpha));
-                o[j][2 * e + 1] = dot2(p23, vhi23[e], dot2(p01, vhi01[e], o[j][2 * e + 1] * alpha));
+                o[j][2 * e] = dot2(p23, vlo23[e], dot2(p01, vlo01[e], o[j][2 * e]));
+                o[j][2 * e + 1] = dot2(p23, vhi23[e], dot2(p01, vhi01[e], o[j][2 * e + 1]));
             }
         }
+    };
+
+    // software pipeline over this wave's blocks (blk_begin + wave, + 4, ...):
+    // the next block's loads are in flight while the current one is consumed;
+    // two register sets alternate so no copies are needed
+    uint4 kA[4], vA[4], kB[4], vB[4];
+    int blk = blk_begin + wave;
+    if (blk < blk_end) load_block(blk, kA, vA);
+    while (blk < blk_end) {
+        int next = blk + kWaves;
+        if (next < blk_end) load_block(next, kB, vB);
+        process(blk, kA, vA);
+        blk = next;
+        if (blk >= blk_end) break;
+        next = blk + kWaves;
+        if (next < blk_end) load_block(next, kA, vA);
+        process(blk, kB, vB);
         blk = next;
     }
 
@@ -311,32 +367,27 @@ void decode_merge_kernel(const float* __restrict__ ws, uint16_t* __restrict__ Op
 }
 
 int heads_per_group(int G) {
-    if (G <= 8) return G;
     if (G % 8 == 0) return 8;
     if (G % 4 == 0) return 4;
     if (G % 2 == 0) return 2;
     return 1;
 }
 
-template <int D, int GH>
+template <int D, int GH, bool NEG>
 void launch_split(const DecodeArgs& a, int ps_log2, float c2, hipStream_t stream) {
     const int groups = a.Hkv * ((a.Hq / a.Hkv) / GH);
-    hipLaunchKernelGGL((decode_split_kernel<D, GH>), dim3(a.nsplit, groups, a.B), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((decode_split_kernel<D, GH, NEG>), dim3(a.nsplit, groups, a.B), dim3(kThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k_pool, (const uint16_t*)a.v_pool,
                        a.page_table, a.seq_lens, a.ws, a.Hq, a.Hkv, ps_log2, a.nsplit, c2);
 }
 
-template <int D>
+template <int D, bool NEG>
 void launch_split_d(const DecodeArgs& a, int GH, int ps_log2, float c2, hipStream_t stream) {
     switch (GH) {
-        case 8: launch_split<D, 8>(a, ps_log2, c2, stream); break;
-        case 7: launch_split<D, 7>(a, ps_log2, c2, stream); break;
-        case 6: launch_split<D, 6>(a, ps_log2, c2, stream); break;
-        case 5: launch_split<D, 5>(a, ps_log2, c2, stream); break;
-        case 4: launch_split<D, 4>(a, ps_log2, c2, stream); break;
-        case 3: launch_split<D, 3>(a, ps_log2, c2, stream); break;
-        case 2: launch_split<D, 2>(a, ps_log2, c2, stream); break;
-        default: launch_split<D, 1>(a, ps_log2, c2, stream); break;
+        case 8: launch_split<D, 8, NEG>(a, ps_log2, c2, stream); break;
+        case 4: launch_split<D, 4, NEG>(a, ps_log2, c2, stream); break;
+        case 2: launch_split<D, 2, NEG>(a, ps_log2, c2, stream); break;
+        default: launch_split<D, 1, NEG>(a, ps_log2, c2, stream); break;
     }
 }
 
@@ -361,8 +412,14 @@ hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream) {
     while ((1 << ps_log2) < a.page_size) ++ps_log2;
     const float c2 = a.scale * 1.4426950408889634f;
     const int GH = heads_per_group(a.Hq / a.Hkv);
-    if (a.D == 128) launch_split_d<128>(a, GH, ps_log2, c2, stream);
-    else launch_split_d<64>(a, GH, ps_log2, c2, stream);
+    const bool neg = a.scale < 0.f;
+    if (a.D == 128) {
+        if (neg) launch_split_d<128, true>(a, GH, ps_log2, c2, stream);
+        else launch_split_d<128, false>(a, GH, ps_log2, c2, stream);
+    } else {
+        if (neg) launch_split_d<64, true>(a, GH, ps_log2, c2, stream);
+        else launch_split_d<64, false>(a, GH, ps_log2, c2, stream);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.D == 128)
