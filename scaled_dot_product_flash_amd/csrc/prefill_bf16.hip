@@ -173,9 +173,9 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             const int row = u / CPR, phys = u % CPR;
             const int kc = phys ^ kswz(row), vcn = phys ^ vswz(row);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + sl * 1024), 16,
-                                                     ((j0 + row) * D + 8 * kc) * 2, 0, 0, 0);
+                                                     (unsigned)(((j0 + row) * D + 8 * kc) * 2), 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + sl * 1024), 16,
-                                                     ((j0 + row) * D + 8 * vcn) * 2, 0, 0, 0);
+                                                     (unsigned)(((j0 + row) * D + 8 * vcn) * 2), 0, 0, 0);
         }
     };
 
@@ -223,12 +223,13 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             }
         }
 
-        // tile extreme of the raw logits (max, or min for a negative scale)
+        // edge tiles: masked logits become -inf (+inf for a negative scale), so
+        // they never win the extreme and exp2 turns them into exact zeros. The
+        // empty volatile asm keeps this block a real branch: the compiler may
+        // not speculate it into every tile.
         const float masked = NEG ? INFINITY : -INFINITY;
-        uint64_t vis = ~0ull;
-        float mx = masked;
         if (edge) {
-            vis = 0;
+            asm volatile("");
 #pragma unroll
             for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
@@ -237,17 +238,14 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                     bool ok = j < Sk;
                     if (causal) ok = ok && j <= qpos;
                     if (window > 0) ok = ok && j > qpos - window;
-                    vis |= (uint64_t)ok << (16 * kbk + v);
-                    const float x = ok ? sacc[kbk][v] : masked;
-                    mx = NEG ? fminf(mx, x) : fmaxf(mx, x);
+                    sacc[kbk][v] = ok ? sacc[kbk][v] : masked;
                 }
-        } else {
-#pragma unroll
-            for (int kbk = 0; kbk < KB; ++kbk)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    mx = NEG ? fminf(mx, sacc[kbk][v]) : fmaxf(mx, sacc[kbk][v]);
         }
+        float mx = masked;
+#pragma unroll
+        for (int kbk = 0; kbk < KB; ++kbk)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mx = NEG ? fminf(mx, sacc[kbk][v]) : fmaxf(mx, sacc[kbk][v]);
         const float other = xor32(mx);
         mx = NEG ? fminf(mx, other) : fmaxf(mx, other);
         const float mt = (mx == masked) ? -INFINITY : mx * c2;
@@ -267,20 +265,14 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                 for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
         }
 
-        // P = exp2(s * c2 - m); masked entries are replaced by exact zeros
-        // (selection, so an overflowing masked logit never matters)
+        // P = exp2(s * c2 - m); a row with no visible key yet subtracts 0
+        // (its logits here are all masked, so every p is exp2(-inf) = 0)
+        const float msub = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
         for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-                sacc[kbk][v] = __builtin_amdgcn_exp2f(fmaf(sacc[kbk][v], c2, -m_run));
-        if (edge) {
-#pragma unroll
-            for (int kbk = 0; kbk < KB; ++kbk)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    sacc[kbk][v] = ((vis >> (16 * kbk + v)) & 1) ? sacc[kbk][v] : 0.f;
-        }
+                sacc[kbk][v] = __builtin_amdgcn_exp2f(fmaf(sacc[kbk][v], c2, -msub));
 
         // bf16 pairs of P as MFMA B operands; l += the same rounded values
         bf16x8 pb[KS];
@@ -361,7 +353,10 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     const long long per_xcd = (nitems + kXcds - 1) / kXcds;
     const long long grid = per_xcd * kXcds;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    const float c2 = a.scale * 1.4426950408889634f;
+    float c2 = a.scale * 1.4426950408889634f;
+    // scale 0: a tiny positive factor gives bit-identical weights (all
+    // exp2(0) = 1 for finite logits) and keeps masked logits at -inf
+    if (c2 == 0.f) c2 = 1e-30f;
     hipLaunchKernelGGL((prefill_bf16_kernel<D, NEG>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
                        a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)per_xcd);
