@@ -36,6 +36,7 @@
 #include "launch.h"
 
 #include <cmath>
+#include <type_traits>
 
 namespace attn {
 namespace {
@@ -46,6 +47,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -346,6 +348,408 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         }
 }
 
+// ---------------------------------------------------------------------------
+// D = 128, software pipelined. Per wave and K/V tile t, one basic block holds
+//  * an S phase of eight chunks: two MFMAs of S(t+1) = K(t+1)·Q^T (their K
+//    operands read from LDS two chunks ahead) beside the exp2 / bf16
+//    conversion of one eighth of P(t), so the matrix and vector units work at
+//    the same time;
+//  * a P·V phase of four chunks: four MFMAs of O^T += V(t)^T·P(t)^T (the
+//    transposing V reads one chunk ahead) beside the mask (boundary tiles
+//    only) and row maximum of S(t+1), and the lazy move of the reference
+//    maximum for tile t+1.
+// The O rescale that a moved maximum asks for runs at the start of the next
+// step, in a branch taken only when some lane of the wave needs it.
+// sched_barrier fences keep the chunks in this order; inside a chunk the
+// compiler interleaves freely. S(t+1) is accumulated 32-key block 1 first,
+// block 0 second, while P(t) consumes block 0 first: only three of the four
+// 16-register blocks of S(t) and S(t+1) are live at any time.
+// K is staged one tile ahead of V: during step t the LDS holds K(t+1) and
+// V(t) while the DMA fills K(t+2) and V(t+1).
+
+__device__ __forceinline__ float2 halves(float x) {
+    // lanes l and l ^ 32 of x, in every lane (v_permlane32_swap)
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x), false, false);
+    return make_float2(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+
+template <int NW, bool NEG>
+__global__ __launch_bounds__(64 * NW, 2)
+void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                         const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                         int Hq, int Hkv, int Sq, int Sk, float c2, int causal, int window,
+                         int nqt, int nitems, int per_xcd) {
+    constexpr int D = 128, BN = 64, KB = 2, KS = 4, DS = 8, DB = 4, CPR = 16;
+    constexpr int TILE_BYTES = BN * D * 2;
+    constexpr int SLOTS = TILE_BYTES / 1024;
+    constexpr int BMW = 32 * NW;  // query rows per workgroup
+    static_assert(SLOTS % NW == 0, "DMA slots per wave");
+
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds1[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds1[TILE_BYTES];
+
+    const int w = blockIdx.x;
+    const int item = (w % kXcds) * per_xcd + w / kXcds;
+    if (item >= nitems) return;
+    const int G = Hq / Hkv;
+    const int hg = item % G;
+    const int r1 = item / G;
+    const int qt = nqt - 1 - (r1 % nqt);
+    const int bg = r1 / nqt;
+    const int g = bg % Hkv;
+    const int b = bg / Hkv;
+    const int h = g * G + hg;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int ln = lane & 31;
+    const int hh = lane >> 5;
+
+    const int off = Sk - Sq;
+    const int i0 = qt * BMW;
+    const int row_end = min(i0 + BMW, Sq);
+
+    const size_t qo_base = ((size_t)b * Hq + h) * (size_t)Sq * D;
+    const size_t kv_base = ((size_t)b * Hkv + g) * (size_t)Sk * D;
+    const int kv_bytes = Sk * D * 2;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(K + kv_base), 0, kv_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(V + kv_base), 0, kv_bytes, kRsrcWord3);
+
+    const int p_first = i0 + off;
+    const int p_last = row_end - 1 + off;
+    const int hi = causal ? min(Sk, p_last + 1) : Sk;
+    const int lo = (causal && window > 0) ? max(0, p_first - window + 1) : 0;
+    const int t_begin = lo / BN;
+    const int t_end = (hi + BN - 1) / BN;
+
+    // Rows of this wave. With eight waves the 32-row blocks are dealt so that
+    // the two waves sharing a SIMD (w and w + 4) hold one early and one late
+    // block: under a causal mask their tile counts then add up to the same
+    // total on every SIMD.
+    const int blk = (NW == 8 && wave >= 4) ? 11 - wave : wave;
+    const int wr0 = i0 + 32 * blk;
+    const int wr1 = min(wr0 + 32, Sq) - 1;
+    const int wp0 = wr0 + off, wp1 = wr1 + off;
+    // tiles wholly visible to all rows of the wave need no mask
+    const int w_full_hi = causal ? min(Sk - 1, wp0) : Sk - 1;
+    const int w_full_lo = (causal && window > 0) ? max(0, wp1 - window + 1) : 0;
+    // last tile with a key visible to the wave (before t_begin: no rows)
+    const int wt_hi = wr0 >= Sq ? t_begin - 1 : (causal ? min(Sk - 1, wp1) / BN : t_end - 1);
+    auto is_edge = [&](int t) __attribute__((always_inline)) { return (t * BN + BN - 1 > w_full_hi) || (t * BN < w_full_lo); };
+
+    const int qrow = wr0 + ln;
+    const int qpos = qrow + off;
+    bf16x8 qreg[DS];
+    {
+        const bool ok = qrow < Sq;
+        const uint16_t* qp = Q + qo_base + (size_t)(ok ? qrow : 0) * D + 8 * hh;
+#pragma unroll
+        for (int st = 0; st < DS; ++st) {
+            uint4 x = ok ? ld_global16(qp + 16 * st) : make_uint4(0, 0, 0, 0);
+            qreg[st] = as_bf16x8(x);
+        }
+    }
+
+    // K rows keep their 16-byte chunks XOR-swizzled by (row & 15), V rows by
+    // (row & 3) << 2; the DMA realises the swizzle through the source offset
+    // 1 KiB per wave instruction; slot i of a wave covers rows 16i + (4 wave
+    // + lane/16), so the swizzle (low row bits) and the lane's byte offset are
+    // the same for every slot. The whole offset goes in the VGPR operand,
+    // which the buffer range check covers; the row part is made opaque so the
+    // compiler adds it per tile instead of keeping one VGPR per slot.
+    const int dma_row = 4 * wave + (lane >> 4);
+    static_assert(SLOTS / NW >= 1, "DMA slots");
+    const unsigned kv_lane_k = (unsigned)((dma_row * D + 8 * ((lane & 15) ^ (dma_row & 15))) * 2);
+    const unsigned kv_lane_v = (unsigned)((dma_row * D + 8 * ((lane & 15) ^ ((dma_row & 3) << 2))) * 2);
+    auto issue = [&](__amdgpu_buffer_rsrc_t rs, int t, unsigned char* dst, bool is_v) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < SLOTS / NW; ++i) {
+            const int sl = wave + NW * i;
+            unsigned rows = (unsigned)((t * BN + 4 * NW * i) * D * 2);
+#if defined(__HIP_DEVICE_COMPILE__)
+            asm volatile("" : "+s"(rows));
+#endif
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + sl * 1024), 16,
+                                                     (unsigned)((is_v ? kv_lane_v : kv_lane_k) + rows), 0, 0, 0);
+        }
+    };
+    // K operand (A: key = lane % 32) of S-step st, keys 32*kbk .. +31
+    auto kread = [&](const unsigned char* kb, int st, int kbk) __attribute__((always_inline)) -> bf16x8 {
+        const int key = 32 * kbk + ln;
+        const int cc = 2 * st + hh;
+        return as_bf16x8(*reinterpret_cast<const uint4*>(kb + key * (D * 2) + ((cc ^ (key & 15)) << 4)));
+    };
+    // V^T operand of P·V k-step ks, d block db: for k-step ks the S^T
+    // accumulators hand lane half hh the keys 16ks + 4hh + {0..3} and
+    // 16ks + 8 + 4hh + {0..3}; two transposing reads fetch exactly those
+    const int grp = (lane >> 4) & 1;
+    const int e4 = (lane & 15) >> 2;
+    const int q4 = lane & 3;
+    auto vop = [&](const unsigned char* vb, int ks, int db) __attribute__((always_inline)) -> bf16x8 {
+        const int key0 = 16 * ks + 4 * hh + e4;
+        const int d = 32 * db + 16 * grp + 4 * q4;
+        const int o_lo = key0 * (D * 2) + (((d >> 3) ^ ((key0 & 3) << 2)) << 4) + ((d & 7) << 1);
+        const int o_hi = o_lo + 8 * (D * 2);  // key0 + 8 has the same swizzle
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + o_lo));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + o_hi));
+        const s16x8 a8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        return __builtin_bit_cast(bf16x8, a8);
+    };
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
+    // Reference maximum of the scaled logits (log2 units), moved only when a
+    // tile exceeds it by more than kLazy; numerator and denominator share it.
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    float alpha = 1.f;      // O rescale owed for the next tile
+    bool rescale = false;   // wave-uniform: some lane owes one
+    const uint32_t ones = 0x3F803F80u;
+    const float masked = NEG ? INFINITY : -INFINITY;
+
+    // mask of the 8 S values of block kbk, elements 8*half .. +7 (edge tiles)
+    auto mask8 = [&](f32x16& sb, int j0, int kbk, int half) __attribute__((always_inline)) {
+        const int base = j0 + 4 * hh;
+        const int sk_hi = Sk - 1 - base;
+        const int lim_hi = causal ? min(qpos - base, sk_hi) : sk_hi;
+        const int lim_lo = window > 0 ? qpos - window - base : -1;
+#pragma unroll
+        for (int v = 8 * half; v < 8 * half + 8; ++v) {
+            const int c = 32 * kbk + 8 * (v >> 2) + (v & 3);
+            const bool ok = c <= lim_hi && c > lim_lo;
+            sb[v] = ok ? sb[v] : masked;
+        }
+    };
+    auto ext8 = [&](const f32x16& sb, int half, float mx) __attribute__((always_inline)) {
+#pragma unroll
+        for (int v = 8 * half; v < 8 * half + 8; ++v) mx = NEG ? fminf(mx, sb[v]) : fmaxf(mx, sb[v]);
+        return mx;
+    };
+    // after the row extreme of a tile: lazy move of the reference maximum
+    auto settle = [&](float mx) __attribute__((always_inline)) {
+        const float2 hv = halves(mx);
+        mx = NEG ? fminf(hv.x, hv.y) : fmaxf(hv.x, hv.y);
+        const float mt = (mx == masked) ? -INFINITY : mx * c2;
+        const bool need = mt > m_run + kLazy;
+        // lanes that keep their reference scale by 1 (m_run may be -inf
+        // there, and -inf - -inf would be NaN); a first finite maximum scales
+        // by exp2(-inf) = 0, which only clears zeros
+        alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
+        m_run = need ? mt : m_run;
+        l_run *= alpha;
+        rescale = __builtin_amdgcn_ballot_w64(need) != 0;
+    };
+    auto apply_rescale = [&]() __attribute__((always_inline)) {
+        if (rescale) {
+            asm volatile("");
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+        }
+    };
+
+    // One pipeline step: P(t) from scur, O += P(t)·V(t) from vb and, if NEXT,
+    // S(t+1) from kb into snew; returns the extreme of the unmasked S(t+1).
+    auto main_block = [&](auto next_c, const unsigned char* kb, const unsigned char* vb,
+                          f32x16 (&scur)[KB], f32x16 (&snew)[KB]) __attribute__((always_inline)) {
+        constexpr bool NEXT = decltype(next_c)::value;
+        apply_rescale();
+        const float msub = (m_run == -INFINITY) ? 0.f : m_run;
+        float la = l_run, lb = 0.f;
+        bf16x8 pb[KS];
+        bf16x8 kr[4];
+        bf16x8 vr[2][DB];
+        // S(t+1) chunk c: block 1 - c/4, S-steps 2(c%4) and 2(c%4)+1
+        auto kst = [](int c, int i) __attribute__((always_inline)) { return 2 * (c & 3) + i; };
+        auto kblk = [](int c) __attribute__((always_inline)) { return 1 - (c >> 2); };
+        if constexpr (NEXT) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) kr[i] = kread(kb, kst(0, i), kblk(0));
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (NEXT) {
+                if (c + 1 < 8) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) kr[2 * ((c + 1) & 1) + i] = kread(kb, kst(c + 1, i), kblk(c + 1));
+                }
+                const int kbs = kblk(c);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const f32x16 zero = {};
+                    snew[kbs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[2 * (c & 1) + i], qreg[kst(c, i)],
+                                                                        ((c & 3) == 0 && i == 0) ? zero : snew[kbs],
+                                                                        0, 0, 0);
+                }
+            }
+            // P(t): k-step ks = c / 2, pairs j = 4*(c%2) and 4*(c%2)+2
+            const int ks = c >> 1, kbk = ks >> 1;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j = 4 * (c & 1) + 2 * jj;
+                const int v0 = 8 * (ks & 1) + j;
+                f32x2 pr = {__builtin_amdgcn_exp2f(fmaf(scur[kbk][v0], c2, -msub)),
+                            __builtin_amdgcn_exp2f(fmaf(scur[kbk][v0 + 1], c2, -msub))};
+                const bf16x2 pbf = __builtin_convertvector(pr, bf16x2);
+                if (jj) lb = __builtin_amdgcn_fdot2_f32_bf16(pbf, __builtin_bit_cast(bf16x2, ones), lb, false);
+                else la = __builtin_amdgcn_fdot2_f32_bf16(pbf, __builtin_bit_cast(bf16x2, ones), la, false);
+                pb[ks][j] = pbf[0];
+                pb[ks][j + 1] = pbf[1];
+            }
+            if (c >= 6) {
+#pragma unroll
+                for (int db = 2 * (c - 6); db < 2 * (c - 6) + 2; ++db) vr[0][db] = vop(vb, 0, db);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        l_run = la + lb;
+        float mx = masked;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[ks & 1][db], pb[ks], oacc[db], 0, 0, 0);
+                if (ks + 1 < KS) vr[(ks + 1) & 1][db] = vop(vb, ks + 1, db);
+            }
+            if constexpr (NEXT) {
+                // S(t+1) block 1 (finished mid S phase) first, block 0 last
+                const int kbk = 1 - (ks >> 1), half = ks & 1;
+                mx = ext8(snew[kbk], half, mx);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        return mx;
+    };
+    // mask of a boundary tile, then its extreme
+    auto edge_extreme = [&](f32x16 (&sb)[KB], int j0) __attribute__((always_inline)) {
+        asm volatile("");
+        float mx = masked;
+#pragma unroll
+        for (int kbk = 0; kbk < KB; ++kbk) {
+            mask8(sb[kbk], j0, kbk, 0);
+            mask8(sb[kbk], j0, kbk, 1);
+            mx = ext8(sb[kbk], 1, ext8(sb[kbk], 0, mx));
+        }
+        return mx;
+    };
+
+    using T = std::integral_constant<bool, true>;
+    using F = std::integral_constant<bool, false>;
+    auto step = [&](int t, const unsigned char* kb, const unsigned char* vb, unsigned char* kdst,
+                    unsigned char* vdst, f32x16 (&scur)[KB], f32x16 (&snew)[KB]) __attribute__((always_inline)) {
+        if (t + 2 < t_end) issue(krs, t + 2, kdst, false);
+        issue(vrs, t + 1, vdst, true);
+        float mx = main_block(T{}, kb, vb, scur, snew);
+        if (is_edge(t + 1)) mx = edge_extreme(snew, (t + 1) * BN);
+        settle(mx);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+    // the wave's last tile u (V(u) in vb): P(u)·V(u) only
+    auto last_step = [&](int u, const unsigned char* vb, unsigned char* kdst, unsigned char* vdst,
+                         f32x16 (&scur)[KB]) __attribute__((always_inline)) {
+        if (u + 2 < t_end) issue(krs, u + 2, kdst, false);
+        if (u + 1 < t_end) issue(vrs, u + 1, vdst, true);
+        main_block(F{}, k_lds0, vb, scur, scur);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+    // a step after the wave's last tile: its share of the DMA and the barrier
+    auto idle_step = [&](int u) __attribute__((always_inline)) {
+        const bool odd = (u - t_begin) & 1;
+        if (u + 2 < t_end) issue(krs, u + 2, odd ? k_lds1 : k_lds0, false);
+        if (u + 1 < t_end) issue(vrs, u + 1, odd ? v_lds0 : v_lds1, true);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+
+    // A wave stops computing after its last visible tile (it still issues its
+    // share of the DMA and meets every barrier). Waves whose rows start after
+    // the group's first tiles compute those fully masked tiles, which add
+    // exact zeros.
+    f32x16 sA[KB], sB[KB];
+    issue(krs, t_begin, k_lds0, false);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t_begin + 1 < t_end) issue(krs, t_begin + 1, k_lds1, false);
+    issue(vrs, t_begin, v_lds0, true);
+    {
+#pragma unroll
+        for (int st = 0; st < DS; ++st)
+#pragma unroll
+            for (int kbk = 0; kbk < KB; ++kbk) {
+                const f32x16 zero = {};
+                sA[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(k_lds0, st, kbk), qreg[st],
+                                                                  st == 0 ? zero : sA[kbk], 0, 0, 0);
+            }
+        float mx = masked;
+#pragma unroll
+        for (int kbk = 0; kbk < KB; ++kbk) mx = ext8(sA[kbk], 1, ext8(sA[kbk], 0, mx));
+        if (is_edge(t_begin)) mx = edge_extreme(sA, t_begin * BN);
+        settle(mx);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // tile t: K(t+1) in k_lds[(t - t_begin + 1) & 1], V(t) in v_lds[(t - t_begin) & 1]
+    int t = t_begin;
+    if (wt_hi >= t_begin) {
+        for (; t + 1 < wt_hi; t += 2) {
+            step(t, k_lds1, v_lds0, k_lds0, v_lds1, sA, sB);
+            step(t + 1, k_lds0, v_lds1, k_lds1, v_lds0, sB, sA);
+        }
+        if (t < wt_hi) {
+            step(t, k_lds1, v_lds0, k_lds0, v_lds1, sA, sB);
+            last_step(t + 1, v_lds1, k_lds1, v_lds0, sB);
+            t += 2;
+        } else {
+            last_step(t, v_lds0, k_lds0, v_lds1, sA);
+            t += 1;
+        }
+    }
+    for (; t < t_end; ++t) idle_step(t);
+
+    if (qrow >= Sq) return;
+    const float2 lh = halves(l_run);
+    const float inv = 1.f / (lh.x + lh.y);
+    uint16_t* op = O + qo_base + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            f32x2 a = {oacc[db][4 * r + 0] * inv, oacc[db][4 * r + 1] * inv};
+            f32x2 c = {oacc[db][4 * r + 2] * inv, oacc[db][4 * r + 3] * inv};
+            uint2 st;
+            st.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2));
+            st.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(c, bf16x2));
+            *reinterpret_cast<uint2*>(op + 32 * db + 8 * r + 4 * hh) = st;
+        }
+}
+
+template <int NW, bool NEG>
+hipError_t launch_pipe(const PrefillArgs& a, hipStream_t stream) {
+    const int nqt = (a.Sq + 32 * NW - 1) / (32 * NW);
+    const long long nitems = (long long)a.B * a.Hq * nqt;
+    const long long per_xcd = (nitems + kXcds - 1) / kXcds;
+    const long long grid = per_xcd * kXcds;
+    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    float c2 = a.scale * 1.4426950408889634f;
+    if (c2 == 0.f) c2 = 1e-30f;
+    hipLaunchKernelGGL((prefill_pipe_kernel<NW, NEG>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
+                       a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)per_xcd);
+    return hipGetLastError();
+}
+
 template <int D, bool NEG>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     const int nqt = (a.Sq + kBM - 1) / kBM;
@@ -367,7 +771,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     const bool neg = a.scale < 0.f;
-    if (a.D == 128) return neg ? launch_t<128, true>(a, stream) : launch_t<128, false>(a, stream);
+    if (a.D == 128) return neg ? launch_pipe<8, true>(a, stream) : launch_pipe<8, false>(a, stream);
     return neg ? launch_t<64, true>(a, stream) : launch_t<64, false>(a, stream);
 }
 
