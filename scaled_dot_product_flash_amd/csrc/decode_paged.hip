@@ -16,7 +16,9 @@
 //    share a K/V head (up to 8) are packed into one workgroup so each page is
 //    read once for all of them. The sequence's context is cut into `nsplit`
 //    contiguous runs of 16-token (D=128) or 32-token (D=64) blocks; the four
-//    waves of a workgroup take the run's blocks round-robin.
+//    waves of a workgroup take the run's blocks round-robin. Grid slot z takes
+//    the sequence of z-th largest length (up to 256 sequences), so the
+//    longest work is dispatched first and the tail of the grid is short.
 //  * A block is read with four 16-byte loads per lane per tensor; lane l holds
 //    d-chunk l % (D/8) of token l / (D/8) (+ 4 or 8 per load), so every load
 //    instruction reads 1 KiB of one page contiguously. The next block's loads
@@ -116,7 +118,29 @@ void decode_split_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __rest
 
     const int split = blockIdx.x;
     const int hgrp = blockIdx.y;        // (kv head, head group)
-    const int b = blockIdx.z;
+    __shared__ int sh_len[kThreads];
+    __shared__ int sh_b;
+    int b = blockIdx.z;
+    {
+        // longest sequences first: slot z of the grid takes the sequence of
+        // length rank z (ties by index), so the long work items start early
+        const int B = gridDim.z;
+        if (B <= kThreads) {
+            if ((int)threadIdx.x < B) sh_len[threadIdx.x] = lens[threadIdx.x];
+            __syncthreads();
+            if ((int)threadIdx.x < B) {
+                const int my = sh_len[threadIdx.x];
+                int rank = 0;
+                for (int j = 0; j < B; ++j) {
+                    const int lj = sh_len[j];
+                    rank += (lj > my) || (lj == my && j < (int)threadIdx.x);
+                }
+                if (rank == (int)blockIdx.z) sh_b = threadIdx.x;
+            }
+            __syncthreads();
+            b = sh_b;
+        }
+    }
     const int G = Hq / Hkv;
     const int groups_per_kv = G / GH;
     const int g = hgrp / groups_per_kv;
@@ -396,7 +420,7 @@ void launch_split_d(const DecodeArgs& a, int GH, int ps_log2, float c2, hipStrea
 int decode_nsplit(int B, int Hq, int Hkv, int num_cu) {
     const int G = Hq / Hkv;
     const long long units = (long long)B * Hkv * (G / heads_per_group(G));
-    const long long target = 16LL * (num_cu > 0 ? num_cu : 256);
+    const long long target = 8LL * (num_cu > 0 ? num_cu : 256);
     long long n = (target + units - 1) / units;
     if (n < 1) n = 1;
     if (n > 64) n = 64;

@@ -566,67 +566,73 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         float la = l_run, lb = 0.f;
         bf16x8 pb[KS];
         bf16x8 kr[4];
-        bf16x8 vr[2][DB];
-        // S(t+1) chunk c: block 1 - c/4, S-steps 2(c%4) and 2(c%4)+1
+        bf16x8 vr[2][2];
+        float mx = masked;
+        // Ten chunks. Chunk c < 8: the two MFMAs of S(t+1) for block 1 - c/4,
+        // S-steps 2(c%4) and 2(c%4)+1 (K read one chunk ahead), and one eighth
+        // of P(t). From chunk 2 on, two P(t)·V(t) MFMAs per chunk (P·V step
+        // (c-2)/2, d blocks 2((c-2)%2) and 2((c-2)%2)+1, V read one chunk
+        // ahead). The extreme of S(t+1) block 1 runs in chunks 6-7, block 0
+        // (whose last MFMA issues in chunk 7) in chunk 9.
         auto kst = [](int c, int i) __attribute__((always_inline)) { return 2 * (c & 3) + i; };
         auto kblk = [](int c) __attribute__((always_inline)) { return 1 - (c >> 2); };
+        auto vread2 = [&](int c, bf16x8 (&dst)[2]) __attribute__((always_inline)) {
+            const int ks = (c - 2) >> 1, db0 = 2 * ((c - 2) & 1);
+            dst[0] = vop(vb, ks, db0);
+            dst[1] = vop(vb, ks, db0 + 1);
+        };
         if constexpr (NEXT) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) kr[i] = kread(kb, kst(0, i), kblk(0));
         }
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        for (int c = 0; c < 10; ++c) {
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (NEXT) {
                 if (c + 1 < 8) {
 #pragma unroll
                     for (int i = 0; i < 2; ++i) kr[2 * ((c + 1) & 1) + i] = kread(kb, kst(c + 1, i), kblk(c + 1));
                 }
-                const int kbs = kblk(c);
+                if (c < 8) {
+                    const int kbs = kblk(c);
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const f32x16 zero = {};
-                    snew[kbs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[2 * (c & 1) + i], qreg[kst(c, i)],
-                                                                        ((c & 3) == 0 && i == 0) ? zero : snew[kbs],
-                                                                        0, 0, 0);
+                    for (int i = 0; i < 2; ++i) {
+                        const f32x16 zero = {};
+                        snew[kbs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[2 * (c & 1) + i], qreg[kst(c, i)],
+                                                                            ((c & 3) == 0 && i == 0) ? zero : snew[kbs],
+                                                                            0, 0, 0);
+                    }
                 }
             }
-            // P(t): k-step ks = c / 2, pairs j = 4*(c%2) and 4*(c%2)+2
-            const int ks = c >> 1, kbk = ks >> 1;
+            if (c + 1 >= 2 && c + 1 < 10) vread2(c + 1, vr[(c + 1) & 1]);
+            if (c >= 2) {
+                const int ks = (c - 2) >> 1, db0 = 2 * ((c - 2) & 1);
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int j = 4 * (c & 1) + 2 * jj;
-                const int v0 = 8 * (ks & 1) + j;
-                f32x2 pr = {__builtin_amdgcn_exp2f(fmaf(scur[kbk][v0], c2, -msub)),
-                            __builtin_amdgcn_exp2f(fmaf(scur[kbk][v0 + 1], c2, -msub))};
-                const bf16x2 pbf = __builtin_convertvector(pr, bf16x2);
-                if (jj) lb = __builtin_amdgcn_fdot2_f32_bf16(pbf, __builtin_bit_cast(bf16x2, ones), lb, false);
-                else la = __builtin_amdgcn_fdot2_f32_bf16(pbf, __builtin_bit_cast(bf16x2, ones), la, false);
-                pb[ks][j] = pbf[0];
-                pb[ks][j + 1] = pbf[1];
+                for (int i = 0; i < 2; ++i)
+                    oacc[db0 + i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[c & 1][i], pb[ks], oacc[db0 + i], 0, 0, 0);
             }
-            if (c >= 6) {
+            if (c < 8) {
+                // P(t): k-step ks = c / 2, pairs j = 4*(c%2) and 4*(c%2)+2
+                const int ks = c >> 1, kbk = ks >> 1;
 #pragma unroll
-                for (int db = 2 * (c - 6); db < 2 * (c - 6) + 2; ++db) vr[0][db] = vop(vb, 0, db);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        l_run = la + lb;
-        float mx = masked;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[ks & 1][db], pb[ks], oacc[db], 0, 0, 0);
-                if (ks + 1 < KS) vr[(ks + 1) & 1][db] = vop(vb, ks + 1, db);
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int j = 4 * (c & 1) + 2 * jj;
+                    const int v0 = 8 * (ks & 1) + j;
+                    f32x2 pr = {__builtin_amdgcn_exp2f(fmaf(scur[kbk][v0], c2, -msub)),
+                                __builtin_amdgcn_exp2f(fmaf(scur[kbk][v0 + 1], c2, -msub))};
+                    const bf16x2 pbf = __builtin_convertvector(pr, bf16x2);
+                    if (jj) lb = __builtin_amdgcn_fdot2_f32_bf16(pbf, __builtin_bit_cast(bf16x2, ones), lb, false);
+                    else la = __builtin_amdgcn_fdot2_f32_bf16(pbf, __builtin_bit_cast(bf16x2, ones), la, false);
+                    pb[ks][j] = pbf[0];
+                    pb[ks][j + 1] = pbf[1];
+                }
             }
             if constexpr (NEXT) {
-                // S(t+1) block 1 (finished mid S phase) first, block 0 last
-                const int kbk = 1 - (ks >> 1), half = ks & 1;
-                mx = ext8(snew[kbk], half, mx);
+                if (c == 6 || c == 7) mx = ext8(snew[1], c - 6, mx);
+                if (c == 9) mx = ext8(snew[0], 1, ext8(snew[0], 0, mx));
             }
         }
+        l_run = la + lb;
         __builtin_amdgcn_sched_barrier(0);
         return mx;
     };
