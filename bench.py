@@ -209,7 +209,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": _traffic("prefill_bf16_kernel", os.path.join(csrc_dir, "prefill_bf16.hip")),
+            "traffic": _traffic("prefill_pipe_kernel", os.path.join(csrc_dir, "prefill_bf16.hip")),
         },
         "decode": {
             "value": round(d_gbps, 2),

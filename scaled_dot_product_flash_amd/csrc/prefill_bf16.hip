@@ -11,21 +11,21 @@
 // row maximum and row sum are kept, earlier partial output is rescaled when
 // the maximum grows, and only O is written back).
 //
-// gfx950 mapping, per workgroup of 4 waves (256 threads):
-//  * 128 query rows, 32 per wave. Each wave computes S^T = K_tile · Q^T with
+// Two kernels share the gfx950 mapping below: prefill_pipe_kernel (D = 128,
+// eight waves and 256 query rows per workgroup, software pipelined, described
+// above its definition) and prefill_bf16_kernel (D = 64, four waves and 128
+// rows). Common to both:
+//  * 32 query rows per wave. Each wave computes S^T = K_tile · Q^T with
 //    v_mfma_f32_32x32x16_bf16, so a lane owns one query column and 16 key
 //    rows of each 32-key block; the row maximum of a query is a reduction
 //    over the lane's own values plus one exchange with lane ^ 32.
 //  * Q lives in registers for the whole loop (it is the MFMA B operand).
-//  * K tiles (key-major) and V tiles (stored transposed, d-major) are staged
-//    through LDS, double buffered: the next tile's global loads are issued
-//    before the current tile's MFMAs and written to the other buffer after.
-//    16-byte chunks are XOR-swizzled by row so the MFMA operand reads
-//    (32 rows at one column) hit distinct banks.
+//  * K and V tiles are staged through LDS by buffer->LDS DMA, double
+//    buffered. 16-byte chunks are XOR-swizzled by row so the MFMA operand
+//    reads (32 rows at one column) hit distinct banks.
 //  * O^T = V^T · P^T also runs on MFMA; P^T comes straight from the S^T
-//    accumulators (converted to bf16 in registers) because the V^T tile is
-//    stored with its keys permuted into the order the accumulator layout
-//    hands them out (bits 2 and 3 of the key index swapped).
+//    accumulators (converted to bf16 in registers); the V^T operand is read
+//    from V in its natural layout with the transposing LDS read.
 //  * Tiles wholly outside a wave's causal/window range are skipped; only
 //    tiles that straddle a boundary or the key tail evaluate the mask.
 //  * Work items are ordered (batch, kv head) major, then query tile from the
@@ -70,10 +70,6 @@ __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 constexpr int kRsrcWord3 = 0x00020000;
 // Lazy-rescale threshold for the reference maximum, log2 units.
 constexpr float kLazy = 8.0f;
-
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
-}
 
 template <int D, bool NEG>
 __global__ __launch_bounds__(kThreads, 2)
