@@ -10,8 +10,11 @@ Printed: ONE JSON line on stdout. ``value`` is prefill attention TFLOP/s
 (4·D flop per visible query/key pair) from HIP events around each prefill
 launch; the decode step's KV GB/s (every cached K/V byte once) is reported
 under ``decode``; ``roofline`` is the prefill kernel against the MI355X dense
-bf16 MFMA peak. ``cpu_baseline`` times the float64 oracle on a bounded sample
-of the prefill workload on the host cores. Progress goes to stderr.
+bf16 MFMA peak. ``decode_window`` times the sliding-window decode (window
+4096) on the same cache, outside the timed steps, as KV GB/s over the
+min(len, 4096) most recent tokens of each sequence. ``cpu_baseline`` times the
+float64 oracle on a bounded sample of the prefill workload on the host cores.
+Progress goes to stderr.
 """
 
 import argparse
@@ -31,6 +34,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 PREFILL = "gqa_causal_4k"
 DECODE = "paged_decode"
+WINDOW = 4096               # sliding-window decode measured beside the step
 
 
 def log(msg):
@@ -167,6 +171,21 @@ def main():
     assert torch.isfinite(po.float()).all() and torch.isfinite(do.float()).all()
     log("timing done")
 
+    # sliding-window decode on the same cache (outside the timed steps)
+    dwo = torch.empty_like(dq)
+    for _ in range(args.warmup):
+        attn.decode_paged_window(dq, dkp, dvp, dpt, dsl, WINDOW, scale=d_scale, o=dwo)
+    win_ms = []
+    for _ in range(args.steps):
+        attn.fwd(pq, pk, pv, o=po, scale=p_scale, causal=True, window=0)  # same cache state as a step
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        attn.decode_paged_window(dq, dkp, dvp, dpt, dsl, WINDOW, scale=d_scale, o=dwo)
+        e1.record()
+        torch.cuda.synchronize()
+        win_ms.append(e0.elapsed_time(e1))
+    assert torch.isfinite(dwo.float()).all()
+
     import statistics
 
     p_flops = work.prefill_flops(wp["B"], wp["Hq"], wp["Sq"], wp["Sk"], wp["D"], True, 0)
@@ -226,6 +245,15 @@ def main():
                 "traffic": _traffic("decode_split_kernel", os.path.join(csrc_dir, "decode_paged.hip")),
             },
         },
+    }
+    w_bytes = work.decode_window_kv_bytes(dd["seq_lens"].tolist(), wd["Hkv"], wd["D"], WINDOW, 2)
+    w_mean = statistics.fmean(win_ms)
+    w_gbps = w_bytes / (w_mean * 1e-3) / 1e9
+    out["decode_window"] = {
+        "window": WINDOW, "value": round(w_gbps, 2), "unit": "GB/s", "kv_bytes_per_call": w_bytes,
+        "ms_mean": round(w_mean, 5), "ms_median": round(statistics.median(win_ms), 5),
+        "roofline": {"bound": "hbm", "achieved": round(w_gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(w_gbps / PEAK_HBM_GBPS, 4)},
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline (~{args.cpu_seconds:.0f} s of oracle work)")

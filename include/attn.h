@@ -47,7 +47,8 @@ enum {
                                (Sk * D * 4 >= 2^31) */
     ATTN_ERR_HEADS = -3,    /* Hq < 1, Hkv < 1 or Hq % Hkv != 0 */
     ATTN_ERR_HEADDIM = -4,  /* D is not 64 or 128 */
-    ATTN_ERR_MASK = -5,     /* causal not 0/1, window < 0, or window > 0 without causal */
+    ATTN_ERR_MASK = -5,     /* causal not 0/1, window < 0, or (prefill) window > 0
+                               without causal */
     ATTN_ERR_SCALE = -6,    /* scale is NaN or infinite */
     ATTN_ERR_PAGE = -7,     /* page_size is not a power of two in [8, 256] */
     ATTN_ERR_ALIGN = -8,    /* a tensor pointer is not 16-byte aligned */
@@ -121,6 +122,24 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                       const int32_t* page_table, const int32_t* seq_lens,
                       int B, int Hq, int Hkv, int D, int page_size,
                       float scale, void* o, hipStream_t stream);
+
+/*
+ * attn_decode_paged_window — the same decode step restricted to a sliding
+ * window: each sequence's query attends only to its `window` most recent
+ * cached tokens, positions max(0, seq_lens[b] - window) .. seq_lens[b] - 1,
+ * the current token included ("拆开 LLM（二）：手撕注意力", exercise that keeps
+ * only the last 256 cache entries; "LLM 核心技术：Attention 机制的实现与优化",
+ * sliding-window section: each token attends to the W previous ones).
+ *   window: >= 0; 0 means no window (identical to attn_decode_paged), a window
+ *   at least seq_lens[b] sees the whole sequence. window < 0 is
+ *   ATTN_ERR_MASK. Every other argument, layout, precondition and the
+ *   workspace are those of attn_decode_paged; pages wholly before the window
+ *   are never read.
+ */
+int attn_decode_paged_window(const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* page_table, const int32_t* seq_lens,
+                             int B, int Hq, int Hkv, int D, int page_size,
+                             float scale, int window, void* o, hipStream_t stream);
 
 /* attn_strerror — static, never-NULL description of a status code. */
 const char* attn_strerror(int status);

@@ -18,4 +18,5 @@ from .attention import (  # noqa: F401
     sequence_pages,
     gather_sequence,
     decode_paged,
+    decode_paged_window,
 )

@@ -186,3 +186,23 @@ def decode_paged(q, k_pool, v_pool, page_table, seq_lens, page_size, scale):
         qb = np.asarray(q[b], dtype=np.float64)[None, :, None, :]
         out[b] = attention(qb, kb, vb, scale, causal=False, window=0)[0, :, 0, :]
     return out
+
+
+def decode_paged_window(q, k_pool, v_pool, page_table, seq_lens, page_size, scale, window):
+    """decode_paged restricted to the `window` most recent cached tokens,
+    float64 [B, Hq, D]; window 0 means no window.
+
+    The new token sits at position n-1 of a cache of n tokens and sees
+    positions n-window .. n-1 ("拆开 LLM（二）", exercise that keeps only the
+    last 256 cache entries; "LLM 核心技术", sliding-window section). This is
+    the causal, windowed attention of one query placed at the end of the
+    gathered sequence (bottom-right alignment, see `visible`).
+    """
+    B, Hq, D = q.shape
+    out = np.empty((B, Hq, v_pool.shape[3]), dtype=np.float64)
+    for b in range(B):
+        kb = gather_sequence(k_pool, page_table, seq_lens, page_size, b)[None]
+        vb = gather_sequence(v_pool, page_table, seq_lens, page_size, b)[None]
+        qb = np.asarray(q[b], dtype=np.float64)[None, :, None, :]
+        out[b] = attention(qb, kb, vb, scale, causal=True, window=int(window))[0, :, 0, :]
+    return out

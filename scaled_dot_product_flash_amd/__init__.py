@@ -45,6 +45,8 @@ def load_library():
         fn.restype = i32
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp]
     lib.attn_decode_paged.restype = i32
+    lib.attn_decode_paged_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp]
+    lib.attn_decode_paged_window.restype = i32
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_release.argtypes = []
@@ -126,15 +128,9 @@ def fwd_f32(q, k, v, o=None, scale=None, causal=False, window=0):
     return _prefill(load_library().attn_fwd_f32, torch.float32, q, k, v, o, scale, causal, window)
 
 
-def decode_paged(q, k_pool, v_pool, page_table, seq_lens, scale=None, o=None):
-    """One decode step over a paged cache.
-
-    q [B,Hq,D] bf16; k_pool / v_pool [num_pages,Hkv,page_size,D] bf16;
-    page_table int32 (ragged, see include/attn.h); seq_lens [B] int32.
-    """
+def _decode_args(q, k_pool, v_pool, page_table, seq_lens, scale, o):
     import torch
 
-    lib = load_library()
     _need(q, "q", torch.bfloat16)
     _need(k_pool, "k_pool", torch.bfloat16)
     _need(v_pool, "v_pool", torch.bfloat16)
@@ -153,8 +149,36 @@ def decode_paged(q, k_pool, v_pool, page_table, seq_lens, scale=None, o=None):
         raise ValueError("o must have the shape of q")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    return B, Hq, Hkv, D, ps, float(scale), o
+
+
+def decode_paged(q, k_pool, v_pool, page_table, seq_lens, scale=None, o=None):
+    """One decode step over a paged cache.
+
+    q [B,Hq,D] bf16; k_pool / v_pool [num_pages,Hkv,page_size,D] bf16;
+    page_table int32 (ragged, see include/attn.h); seq_lens [B] int32.
+    """
+    import torch
+
+    lib = load_library()
+    B, Hq, Hkv, D, ps, scale, o = _decode_args(q, k_pool, v_pool, page_table, seq_lens, scale, o)
     with torch.cuda.device(q.device):
         rc = lib.attn_decode_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(),
-                                   seq_lens.data_ptr(), B, Hq, Hkv, D, ps, float(scale), o.data_ptr(), _stream(q))
+                                   seq_lens.data_ptr(), B, Hq, Hkv, D, ps, scale, o.data_ptr(), _stream(q))
     _check(rc, "attn_decode_paged")
+    return o
+
+
+def decode_paged_window(q, k_pool, v_pool, page_table, seq_lens, window, scale=None, o=None):
+    """decode_paged restricted to each sequence's `window` most recent tokens
+    (window 0: no restriction)."""
+    import torch
+
+    lib = load_library()
+    B, Hq, Hkv, D, ps, scale, o = _decode_args(q, k_pool, v_pool, page_table, seq_lens, scale, o)
+    with torch.cuda.device(q.device):
+        rc = lib.attn_decode_paged_window(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                          page_table.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, ps, scale,
+                                          int(window), o.data_ptr(), _stream(q))
+    _check(rc, "attn_decode_paged_window")
     return o

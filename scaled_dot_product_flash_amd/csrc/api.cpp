@@ -94,6 +94,36 @@ int cu_count(int device, int* out) {
     return ATTN_OK;
 }
 
+int decode_call(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int page_size, float scale, int window,
+                void* o, hipStream_t stream) {
+    if (B < 0) return ATTN_ERR_SHAPE;
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_HEADS;
+    if (D != 64 && D != 128) return ATTN_ERR_HEADDIM;
+    if (page_size < 8 || page_size > 256 || (page_size & (page_size - 1)) != 0) return ATTN_ERR_PAGE;
+    if (window < 0) return ATTN_ERR_MASK;
+    if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+    if (B == 0) return ATTN_OK;
+    if (B > 65535 || Hq > 65535) return ATTN_ERR_SHAPE;
+    if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !o) return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o) || !aligned4(page_table) ||
+        !aligned4(seq_lens))
+        return ATTN_ERR_ALIGN;
+
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return ATTN_ERR_HIP;
+    int ncu = 0;
+    int rc = cu_count(device, &ncu);
+    if (rc != ATTN_OK) return rc;
+    const int nsplit = attn::decode_nsplit(B, Hq, Hkv, ncu);
+    float* ws = nullptr;
+    rc = get_workspace(device, stream, attn::decode_workspace_floats(B, Hq, D, nsplit), &ws);
+    if (rc != ATTN_OK) return rc;
+    attn::DecodeArgs a{q, k_pool, v_pool, page_table, seq_lens, o, B, Hq, Hkv, D, page_size, scale, window,
+                       nsplit, ws};
+    return hip_status(attn::launch_decode_paged(a, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,29 +149,14 @@ int attn_fwd_f32(const void* q, const void* k, const void* v, void* o, int B, in
 int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
                       const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int page_size, float scale,
                       void* o, hipStream_t stream) {
-    if (B < 0) return ATTN_ERR_SHAPE;
-    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_HEADS;
-    if (D != 64 && D != 128) return ATTN_ERR_HEADDIM;
-    if (page_size < 8 || page_size > 256 || (page_size & (page_size - 1)) != 0) return ATTN_ERR_PAGE;
-    if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
-    if (B == 0) return ATTN_OK;
-    if (B > 65535 || Hq > 65535) return ATTN_ERR_SHAPE;
-    if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !o) return ATTN_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o) || !aligned4(page_table) ||
-        !aligned4(seq_lens))
-        return ATTN_ERR_ALIGN;
+    return decode_call(q, k_pool, v_pool, page_table, seq_lens, B, Hq, Hkv, D, page_size, scale, 0, o, stream);
+}
 
-    int device = 0;
-    if (hipGetDevice(&device) != hipSuccess) return ATTN_ERR_HIP;
-    int ncu = 0;
-    int rc = cu_count(device, &ncu);
-    if (rc != ATTN_OK) return rc;
-    const int nsplit = attn::decode_nsplit(B, Hq, Hkv, ncu);
-    float* ws = nullptr;
-    rc = get_workspace(device, stream, attn::decode_workspace_floats(B, Hq, D, nsplit), &ws);
-    if (rc != ATTN_OK) return rc;
-    attn::DecodeArgs a{q, k_pool, v_pool, page_table, seq_lens, o, B, Hq, Hkv, D, page_size, scale, nsplit, ws};
-    return hip_status(attn::launch_decode_paged(a, stream));
+int attn_decode_paged_window(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                             const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int page_size, float scale,
+                             int window, void* o, hipStream_t stream) {
+    return decode_call(q, k_pool, v_pool, page_table, seq_lens, B, Hq, Hkv, D, page_size, scale, window, o,
+                       stream);
 }
 
 const char* attn_strerror(int status) {
@@ -151,7 +166,7 @@ const char* attn_strerror(int status) {
         case ATTN_ERR_SHAPE: return "invalid size (negative, zero where >= 1 is required, causal with Sq > Sk, or too large)";
         case ATTN_ERR_HEADS: return "invalid head counts (need Hq >= 1, Hkv >= 1, Hq % Hkv == 0)";
         case ATTN_ERR_HEADDIM: return "unsupported head dimension (D must be 64 or 128)";
-        case ATTN_ERR_MASK: return "invalid mask arguments (causal must be 0/1; window >= 0 and only with causal)";
+        case ATTN_ERR_MASK: return "invalid mask arguments (causal must be 0/1; window >= 0, and for prefill only with causal)";
         case ATTN_ERR_SCALE: return "scale is not finite";
         case ATTN_ERR_PAGE: return "page_size must be a power of two in [8, 256]";
         case ATTN_ERR_ALIGN: return "a tensor pointer is not sufficiently aligned (16 bytes; 4 for int32 tables)";

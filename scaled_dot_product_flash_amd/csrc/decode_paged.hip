@@ -33,6 +33,11 @@
 //    the same two tokens, and v_dot2_f32_bf16 accumulates both at once.
 //  * Tokens at or past seq_lens[b] are excluded by selection (logit -inf, V
 //    zeroed), never by multiplying with 0, so NaN padding cannot leak.
+//  * Sliding window (window W > 0): only the W most recent tokens, positions
+//    len-W .. len-1, are visible ("拆开 LLM（二）：手撕注意力", exercise that keeps
+//    the last 256 cache entries; "LLM 核心技术：Attention 机制的实现与优化",
+//    sliding-window section); the splits cover just those blocks and tokens
+//    before len-W in the first block are excluded the same way.
 //  * Merge kernel: per (sequence, query head) combines the split partials
 //    (m, l, o) into the bf16 output.
 
@@ -106,7 +111,7 @@ __global__ __launch_bounds__(kThreads)
 void decode_split_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __restrict__ Kp,
                          const uint16_t* __restrict__ Vp, const int32_t* __restrict__ table,
                          const int32_t* __restrict__ lens, float* __restrict__ ws,
-                         int Hq, int Hkv, int ps_log2, int nsplit, float c2) {
+                         int Hq, int Hkv, int ps_log2, int nsplit, float c2, int window) {
     constexpr int CPT = D / 8;        // lanes per token (16-byte chunks per row)
     constexpr int TPI = 64 / CPT;     // tokens per load instruction
     constexpr int TB = 4 * TPI;       // tokens per block
@@ -164,9 +169,12 @@ void decode_split_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __rest
     const int len = lens[b];
     const int32_t* tab = table + off_b;
 
-    const int nblk = (len + TB - 1) / TB;
-    const int blk_begin = (int)((long long)nblk * split / nsplit);
-    const int blk_end = (int)((long long)nblk * (split + 1) / nsplit);
+    // visible tokens first .. len-1; blocks blk0 .. blk0 + nblk - 1
+    const int first = window > 0 ? max(0, len - window) : 0;
+    const int blk0 = first / TB;
+    const int nblk = (len + TB - 1) / TB - blk0;
+    const int blk_begin = blk0 + (int)((long long)nblk * split / nsplit);
+    const int blk_end = blk0 + (int)((long long)nblk * (split + 1) / nsplit);
 
     // q of the packed heads: 8 dims (4 bf16 pairs) per lane and head
     uint32_t qv[GH][4];
@@ -233,14 +241,16 @@ void decode_split_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __rest
             for (int j = 0; j < GH; ++j) s[i][j] = dot2(qv[j][3], kc[i].w, s[i][j]);
         token_sum_all<CPT, 4 * GH>(&s[0][0]);
 
-        // the block holding the last token: tokens >= len get an extreme
-        // logit that never wins the max, and their V rows become zeros
-        const bool partial = (blk + 1) * TB > len;
+        // blocks at either end of the visible range: tokens at or past len, or
+        // before the window, get an extreme logit that never wins the max, and
+        // their V rows become zeros
+        const bool partial = (blk + 1) * TB > len || blk * TB < first;
         bool ok[4] = {true, true, true, true};
         if (partial) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                ok[i] = blk * TB + i * TPI + r < len;
+                const int tok = blk * TB + i * TPI + r;
+                ok[i] = tok < len && tok >= first;
                 if (!ok[i]) {
 #pragma unroll
                     for (int j = 0; j < GH; ++j) s[i][j] = NEG ? INFINITY : -INFINITY;
@@ -402,7 +412,7 @@ void launch_split(const DecodeArgs& a, int ps_log2, float c2, hipStream_t stream
     const int groups = a.Hkv * ((a.Hq / a.Hkv) / GH);
     hipLaunchKernelGGL((decode_split_kernel<D, GH, NEG>), dim3(a.nsplit, groups, a.B), dim3(kThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k_pool, (const uint16_t*)a.v_pool,
-                       a.page_table, a.seq_lens, a.ws, a.Hq, a.Hkv, ps_log2, a.nsplit, c2);
+                       a.page_table, a.seq_lens, a.ws, a.Hq, a.Hkv, ps_log2, a.nsplit, c2, a.window);
 }
 
 template <int D, bool NEG>

@@ -27,6 +27,7 @@ struct DecodeArgs {
     void* o;
     int B, Hq, Hkv, D, page_size;
     float scale;
+    int window;     // 0: every cached token; W > 0: the W most recent
     int nsplit;     // context splits per (sequence, head group)
     float* ws;      // partial results, decode_workspace_floats() floats
 };

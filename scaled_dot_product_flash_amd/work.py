@@ -58,3 +58,11 @@ def kv_bytes_per_token(Hkv, D, elem_bytes):
 def decode_kv_bytes(seq_lens, Hkv, D, elem_bytes=2):
     """Bytes of valid K/V a decode step must read: every cached token once."""
     return sum(int(n) for n in seq_lens) * kv_bytes_per_token(Hkv, D, elem_bytes)
+
+
+def decode_window_kv_bytes(seq_lens, Hkv, D, window, elem_bytes=2):
+    """Bytes of valid K/V a windowed decode step must read: the min(len, W)
+    most recent tokens of each sequence (W = 0: all of them)."""
+    if window <= 0:
+        return decode_kv_bytes(seq_lens, Hkv, D, elem_bytes)
+    return sum(min(int(n), window) for n in seq_lens) * kv_bytes_per_token(Hkv, D, elem_bytes)

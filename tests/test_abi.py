@@ -39,7 +39,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared() == ["attn_decode_paged", "attn_fwd", "attn_fwd_f32", "attn_release", "attn_strerror"]
+    assert _declared() == ["attn_decode_paged", "attn_decode_paged_window", "attn_fwd", "attn_fwd_f32",
+                           "attn_release", "attn_strerror"]
     assert _codes() == {"ATTN_OK": OK, "ATTN_ERR_NULL": NULL, "ATTN_ERR_SHAPE": SHAPE, "ATTN_ERR_HEADS": HEADS,
                         "ATTN_ERR_HEADDIM": HEADDIM, "ATTN_ERR_MASK": MASK, "ATTN_ERR_SCALE": SCALE,
                         "ATTN_ERR_PAGE": PAGE, "ATTN_ERR_ALIGN": ALIGN, "ATTN_ERR_NOMEM": NOMEM, "ATTN_ERR_HIP": HIP}
@@ -101,8 +102,10 @@ def test_prefill_empty_calls_are_no_ops(lib, f32):
     assert _fwd(lib, q=None, k=None, v=None, o=None, Sq=0, causal=0, f32=f32) == OK
 
 
-def _dec(lib, q=A, kp=A, vp=A, pt=A, sl=A, o=A, B=2, Hq=8, Hkv=2, D=128, ps=16, scale=0.1):
-    return lib.attn_decode_paged(q, kp, vp, pt, sl, B, Hq, Hkv, D, ps, scale, o, None)
+def _dec(lib, q=A, kp=A, vp=A, pt=A, sl=A, o=A, B=2, Hq=8, Hkv=2, D=128, ps=16, scale=0.1, window=None):
+    if window is None:
+        return lib.attn_decode_paged(q, kp, vp, pt, sl, B, Hq, Hkv, D, ps, scale, o, None)
+    return lib.attn_decode_paged_window(q, kp, vp, pt, sl, B, Hq, Hkv, D, ps, scale, window, o, None)
 
 
 @pytest.mark.parametrize("kwargs,code", [
@@ -118,10 +121,19 @@ def _dec(lib, q=A, kp=A, vp=A, pt=A, sl=A, o=A, B=2, Hq=8, Hkv=2, D=128, ps=16, 
 ])
 def test_decode_validation(lib, kwargs, code):
     assert _dec(lib, **kwargs) == code
+    # the windowed entry point validates the same arguments the same way
+    assert _dec(lib, window=5, **kwargs) == code
+
+
+@pytest.mark.parametrize("window", [-1, -100])
+def test_decode_window_validation(lib, window):
+    assert _dec(lib, window=window) == MASK
+    assert _dec(lib, window=window, B=0) == MASK
 
 
 def test_decode_empty_batch_is_a_no_op(lib):
     assert _dec(lib, q=None, kp=None, vp=None, pt=None, sl=None, o=None, B=0) == OK
+    assert _dec(lib, q=None, kp=None, vp=None, pt=None, sl=None, o=None, B=0, window=3) == OK
 
 
 def test_release_without_work_is_a_no_op(lib):
@@ -143,3 +155,4 @@ def test_ctypes_signature_matches_header(lib):
     assert lib.attn_fwd.restype is ctypes.c_int
     assert len(lib.attn_fwd.argtypes) == 14
     assert len(lib.attn_decode_paged.argtypes) == 13
+    assert len(lib.attn_decode_paged_window.argtypes) == 14

@@ -1,4 +1,5 @@
-"""GPU parity of attn_decode_paged against the float64 oracle.
+"""GPU parity of attn_decode_paged and attn_decode_paged_window against the
+float64 oracle.
 
 Padding slots of every sequence's last page hold NaN, so any read of a token
 at or past seq_lens[b] shows up as a non-finite output.
@@ -28,6 +29,19 @@ def _run(d, scale):
 def _oracle(d, scale):
     return oracle.decode_paged(f64(d["q"]), d["k_pool"].float().numpy(), d["v_pool"].float().numpy(),
                                d["page_table"].numpy(), d["seq_lens"].numpy(), d["k_pool"].shape[2], scale)
+
+
+def _run_w(d, scale, window):
+    q, kp, vp, pt, sl = cuda(d["q"], d["k_pool"], d["v_pool"], d["page_table"], d["seq_lens"])
+    o = attn.decode_paged_window(q, kp, vp, pt, sl, window, scale=scale)
+    torch.cuda.synchronize()
+    return o.cpu()
+
+
+def _oracle_w(d, scale, window):
+    return oracle.decode_paged_window(f64(d["q"]), d["k_pool"].float().numpy(), d["v_pool"].float().numpy(),
+                                      d["page_table"].numpy(), d["seq_lens"].numpy(), d["k_pool"].shape[2],
+                                      scale, window)
 
 
 def test_paged_decode_workload():
@@ -145,3 +159,85 @@ def test_repeated_calls_and_streams_agree():
     assert torch.equal(_run(d, 0.1), first)
     attn.release()
     assert torch.equal(_run(d, 0.1), first)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 0.5])
+def test_unusual_scales(scale):
+    d = inputs.decode_inputs(5, 8, 2, 128, 16, 1, 700, "bf16", seed=37)
+    check_bf16(f64(_run(d, scale)), _oracle(d, scale), f"scale {scale}")
+    check_bf16(f64(_run_w(d, scale, 100)), _oracle_w(d, scale, 100), f"window 100, scale {scale}")
+
+
+# ---- sliding-window decode ------------------------------------------------------
+
+def test_window_decode_workload():
+    # the 64-sequence workload with a 4096-token window (about half of the
+    # sequences are longer than the window)
+    w = inputs.WORKLOADS["paged_decode"]
+    say("window decode workload paged_decode, window 4096")
+    d = inputs.workload_inputs("paged_decode")
+    scale = 1.0 / math.sqrt(w["D"])
+    check_bf16(f64(_run_w(d, scale, 4096)), _oracle_w(d, scale, 4096), "paged_decode window 4096")
+
+
+WINDOW_CASES = [
+    # nseq, Hq, Hkv, D, page_size, lens, window
+    (4, 8, 2, 128, 16, [15, 16, 17, 33], 1),
+    (4, 8, 2, 128, 16, [15, 16, 17, 33], 16),
+    (5, 32, 8, 128, 16, [500, 1, 64, 63, 1000], 17),
+    (3, 4, 4, 64, 8, [1, 8, 9], 2),
+    (3, 12, 12, 64, 64, [130, 64, 1], 100),
+    (2, 16, 1, 128, 32, [700, 5], 256),     # MQA
+    (2, 8, 2, 128, 256, [300, 1000], 333),
+    (6, 8, 2, 128, 16, [3000, 2048, 4097, 17, 5000, 100], 2048),
+    (64, 4, 2, 128, 16, list(range(1, 65)), 7),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES)
+def test_window_decode_cases(case):
+    nseq, Hq, Hkv, D, ps, lens, window = case
+    say(f"window decode {case}")
+    d = inputs.decode_inputs(nseq, Hq, Hkv, D, ps, 0, 0, "bf16", seed=sum(lens) % 1000 + window, seq_lens=lens)
+    scale = 1.0 / math.sqrt(D)
+    check_bf16(f64(_run_w(d, scale, window)), _oracle_w(d, scale, window), str(case))
+
+
+def test_window_zero_and_wide_windows_equal_plain_decode_bit_exact():
+    d = inputs.decode_inputs(6, 8, 2, 128, 16, 1, 900, "bf16", seed=38)
+    plain = _run(d, 0.1)
+    assert torch.equal(_run_w(d, 0.1, 0), plain)
+    # a window at least as long as every sequence covers the same blocks
+    assert torch.equal(_run_w(d, 0.1, 900), plain)
+
+
+def test_window_one_is_the_last_value_row_exactly():
+    d = inputs.decode_inputs(5, 8, 2, 128, 16, 1, 300, "bf16", seed=39)
+    got = _run_w(d, 0.1, 1)
+    first = 0
+    for b, n in enumerate(d["seq_lens"].tolist()):
+        c = (n + 15) // 16
+        page = int(d["page_table"][first + (n - 1) // 16])
+        vrow = d["v_pool"][page, :, (n - 1) % 16]             # [Hkv, D]
+        assert torch.equal(got[b], vrow.repeat_interleave(4, dim=0)), b
+        first += c
+
+
+def test_window_decode_equals_last_windowed_prefill_row():
+    S, Hq, Hkv, D, ps, W = 300, 8, 2, 128, 16, 37
+    q, k, v = inputs.prefill_inputs(1, Hq, Hkv, S, S, D, "bf16", 40)
+    scale = 1.0 / math.sqrt(D)
+    full = attn.fwd(*cuda(q, k, v), scale=scale, causal=True, window=W).cpu()
+    for t in (1, 36, 37, 38, 150, 300):
+        n_pages = (t + ps - 1) // ps
+        kp = torch.zeros(n_pages * ps, Hkv, D, dtype=torch.bfloat16)
+        vp = torch.zeros_like(kp)
+        kp[:t] = k[0, :, :t].transpose(0, 1)
+        vp[:t] = v[0, :, :t].transpose(0, 1)
+        kp = kp.view(n_pages, ps, Hkv, D).transpose(1, 2).contiguous()
+        vp = vp.view(n_pages, ps, Hkv, D).transpose(1, 2).contiguous()
+        d = dict(q=q[0, :, t - 1][None].contiguous(), k_pool=kp, v_pool=vp,
+                 page_table=torch.arange(n_pages, dtype=torch.int32), seq_lens=torch.tensor([t], dtype=torch.int32))
+        step = _run_w(d, scale, W)
+        check_bf16(f64(step[0]), f64(full[0, :, t - 1]), f"t={t}")
+        check_bf16(f64(step), _oracle_w(d, scale, W), f"t={t} vs oracle")

@@ -339,3 +339,62 @@ def test_visible_rejects_window_without_causal():
 
 def test_sequence_pages_layout():
     assert oracle.sequence_pages([1, 16, 17, 32], 16) == [(0, 1), (1, 1), (2, 2), (4, 2)]
+
+
+# ----------------------------------------------------------------------------
+# sliding-window decode
+
+
+@pytest.mark.parametrize("window", [1, 3, 8, 16, 50])
+def test_window_decode_matches_brute_force(window):
+    # the new token at position n-1 sees positions max(0, n-window) .. n-1
+    rng = np.random.default_rng(12)
+    lens = [1, 5, 9, 16, 23]
+    B, Hq, Hkv, D, ps = len(lens), 4, 2, 3, 8
+    Smax = max(lens)
+    kc = rng.standard_normal((B, Hkv, Smax, D))
+    vc = rng.standard_normal((B, Hkv, Smax, D))
+    q = rng.standard_normal((B, Hq, D))
+    kp, vp, table = _paged_from_contiguous(kc, vc, lens, ps, rng, True)
+    got = oracle.decode_paged_window(q, kp, vp, table, np.array(lens), ps, 0.7, window)
+    for b, n in enumerate(lens):
+        want = _brute(q[b:b + 1, :, None, :].tolist(), kc[b:b + 1, :, :n].tolist(),
+                      vc[b:b + 1, :, :n].tolist(), 0.7, True, window)
+        np.testing.assert_allclose(got[b], want[0, :, 0, :], atol=1e-12)
+
+
+def test_window_decode_position_probe():
+    # Q = 0 -> mean over the window of the bits of the token index
+    rng = np.random.default_rng(13)
+    lens, ps, nbits, W = [3, 16, 33, 100], 16, 7, 20
+    B, Hkv = len(lens), 2
+    Smax = max(lens)
+    kc = rng.standard_normal((B, Hkv, Smax, nbits))
+    bits = ((np.arange(Smax)[:, None] >> np.arange(nbits)[None, :]) & 1).astype(np.float64)
+    vc = np.broadcast_to(bits, (B, Hkv, Smax, nbits)).copy()
+    kp, vp, table = _paged_from_contiguous(kc, vc, lens, ps, rng, True)
+    got = oracle.decode_paged_window(np.zeros((B, 4, nbits)), kp, vp, table, np.array(lens), ps, 1.0, W)
+    for b, n in enumerate(lens):
+        lo = max(0, n - W)
+        want = [(_count_bit_below(n, c) - _count_bit_below(lo, c)) / (n - lo) for c in range(nbits)]
+        np.testing.assert_allclose(got[b], np.broadcast_to(want, (4, nbits)), atol=1e-12)
+
+
+def test_window_decode_special_cases():
+    rng = np.random.default_rng(14)
+    lens = [1, 7, 30]
+    B, Hq, Hkv, D, ps = len(lens), 2, 1, 5, 8
+    Smax = max(lens)
+    kc = rng.standard_normal((B, Hkv, Smax, D))
+    vc = rng.standard_normal((B, Hkv, Smax, D))
+    q = rng.standard_normal((B, Hq, D))
+    kp, vp, table = _paged_from_contiguous(kc, vc, lens, ps, rng, True)
+    sl = np.array(lens)
+    full = oracle.decode_paged(q, kp, vp, table, sl, ps, 0.4)
+    # no window, or a window at least as long as every sequence: plain decode
+    for W in (0, 30, 1000):
+        np.testing.assert_allclose(oracle.decode_paged_window(q, kp, vp, table, sl, ps, 0.4, W), full, atol=1e-14)
+    # a window of one token returns that token's V row
+    one = oracle.decode_paged_window(q, kp, vp, table, sl, ps, 0.4, 1)
+    for b, n in enumerate(lens):
+        np.testing.assert_allclose(one[b], np.broadcast_to(vc[b, 0, n - 1], (Hq, D)), atol=1e-15)

@@ -57,3 +57,16 @@ def test_workload_flops_match_closed_forms():
 def test_decode_bytes():
     lens = np.array([512, 8192, 1000])
     assert work.decode_kv_bytes(lens, 8, 128) == int(lens.sum()) * 2 * 8 * 128 * 2
+
+
+def test_decode_window_bytes():
+    from scaled_dot_product_flash_amd import work
+
+    lens = [1, 100, 4096, 5000]
+    per = work.kv_bytes_per_token(8, 128, 2)
+    assert work.decode_window_kv_bytes(lens, 8, 128, 0) == work.decode_kv_bytes(lens, 8, 128)
+    assert work.decode_window_kv_bytes(lens, 8, 128, 4096) == (1 + 100 + 4096 + 4096) * per
+    assert work.decode_window_kv_bytes(lens, 8, 128, 1) == 4 * per
+    # the windowed pair count of one query at the end of n keys is min(n, W)
+    for n in lens:
+        assert work.visible_pairs(1, n, True, 4096) == min(n, 4096)
