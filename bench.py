@@ -12,7 +12,8 @@ launch; the decode step's KV GB/s (every cached K/V byte once) is reported
 under ``decode``; ``roofline`` is the prefill kernel against the MI355X dense
 bf16 MFMA peak. ``decode_window`` times the sliding-window decode (window
 4096) on the same cache, outside the timed steps, as KV GB/s over the
-min(len, 4096) most recent tokens of each sequence. ``cpu_baseline`` times the
+min(len, 4096) most recent tokens of each sequence; ``kv_append`` times the
+append of one new token per sequence to the same cache. ``cpu_baseline`` times the
 float64 oracle on a bounded sample of the prefill workload on the host cores.
 Progress goes to stderr.
 """
@@ -186,6 +187,21 @@ def main():
         win_ms.append(e0.elapsed_time(e1))
     assert torch.isfinite(dwo.float()).all()
 
+    # KV append of one new token per sequence (outside the timed steps; it
+    # rewrites the last cached token of each sequence)
+    kn = torch.randn((wd["nseq"], wd["Hkv"], wd["D"]), device=dev).to(torch.bfloat16)
+    vn = torch.randn_like(kn)
+    for _ in range(args.warmup):
+        attn.kv_append(kn, vn, dkp, dvp, dpt, dsl)
+    app_ms = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        attn.kv_append(kn, vn, dkp, dvp, dpt, dsl)
+        e1.record()
+        torch.cuda.synchronize()
+        app_ms.append(e0.elapsed_time(e1))
+
     import statistics
 
     p_flops = work.prefill_flops(wp["B"], wp["Hq"], wp["Sq"], wp["Sk"], wp["D"], True, 0)
@@ -254,6 +270,13 @@ def main():
         "ms_mean": round(w_mean, 5), "ms_median": round(statistics.median(win_ms), 5),
         "roofline": {"bound": "hbm", "achieved": round(w_gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(w_gbps / PEAK_HBM_GBPS, 4)},
+    }
+    a_bytes = 2 * 2 * wd["nseq"] * wd["Hkv"] * wd["D"] * 2   # k_new, v_new read; two slots written
+    a_med = statistics.median(app_ms)
+    out["kv_append"] = {
+        "us_median": round(a_med * 1e3, 2), "us_mean": round(statistics.fmean(app_ms) * 1e3, 2),
+        "bytes_per_call": a_bytes, "GBps": round(a_bytes / (a_med * 1e-3) / 1e9, 2),
+        "note": "latency-bound: a few KiB per sequence, one workgroup per sequence",
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline (~{args.cpu_seconds:.0f} s of oracle work)")

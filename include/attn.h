@@ -53,7 +53,9 @@ enum {
     ATTN_ERR_PAGE = -7,     /* page_size is not a power of two in [8, 256] */
     ATTN_ERR_ALIGN = -8,    /* a tensor pointer is not 16-byte aligned */
     ATTN_ERR_NOMEM = -9,    /* the decode workspace could not be allocated */
-    ATTN_ERR_HIP = -10      /* a HIP runtime call or kernel launch failed */
+    ATTN_ERR_HIP = -10,     /* a HIP runtime call or kernel launch failed */
+    ATTN_ERR_FULL = -11,    /* the page pool has too few free pages */
+    ATTN_ERR_SEQ = -12      /* a sequence id the page pool does not hold */
 };
 
 /*
@@ -140,6 +142,68 @@ int attn_decode_paged_window(const void* q, const void* k_pool, const void* v_po
                              const int32_t* page_table, const int32_t* seq_lens,
                              int B, int Hq, int Hkv, int D, int page_size,
                              float scale, int window, void* o, hipStream_t stream);
+
+/*
+ * attn_kv_append — write the new token's k and v into the paged cache, the
+ * step that precedes attention in a decode ("拆开 LLM（二）：手撕注意力",
+ * KV-cache section: the new key and value are appended, then the token
+ * attends to every cached position; "LLM 核心技术", PagedAttention section).
+ *
+ *   k_new, v_new : [B, Hkv, D] bfloat16, one token per sequence.
+ *   k_pool, v_pool, page_table, seq_lens, page_size : as in
+ *                  attn_decode_paged. seq_lens[b] already counts the new
+ *                  token: it is written to position seq_lens[b] - 1, slot
+ *                  (seq_lens[b] - 1) % page_size of physical page
+ *                  page_table[off_b + (seq_lens[b] - 1) / page_size]. Nothing
+ *                  else in the pools changes.
+ *   The page holding that position must already be in the table (see
+ *   attn_pages_resize); the device-side preconditions of attn_decode_paged
+ *   apply. Sequences must not share physical pages.
+ *   Errors: NULL, SHAPE (B < 0), HEADS (Hkv < 1), HEADDIM, PAGE, ALIGN
+ *   (16 bytes for tensors, 4 for the int32 arrays), HIP. B == 0 is a no-op.
+ */
+int attn_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                   const int32_t* page_table, const int32_t* seq_lens,
+                   int B, int Hkv, int D, int page_size, hipStream_t stream);
+
+/*
+ * Page pool — host-side allocator of the physical pages of a paged KV cache
+ * ("LLM 核心技术", PagedAttention section; "Attention From Scratch", paged
+ * KV cache: fixed-size pages from one global pool, handed to sequences on
+ * demand and returned when they shrink or end). Pure host code: no HIP call,
+ * no device memory. Each call locks the pool, so one pool may be shared by
+ * threads. The pool owns no cache memory; it only hands out page ids
+ * 0 .. num_pages - 1 of pools the caller allocates.
+ *
+ * attn_pages_create  — a pool of num_pages (>= 1, else SHAPE) free pages of
+ *                      page_size tokens (power of two in [8, 256], else PAGE);
+ *                      *out receives the handle (NULL out: NULL; NOMEM).
+ * attn_pages_destroy — frees the handle (NULL is a no-op).
+ * attn_pages_resize  — sets sequence seq_id (any int64 key; created on first
+ *                      use) to len >= 0 tokens (SHAPE if negative): it then
+ *                      owns ceil(len / page_size) pages. Missing pages are
+ *                      taken from the free list and appended in logical
+ *                      order; surplus pages leave from the end and return to
+ *                      the free list; len == 0 releases every page and drops
+ *                      the sequence. FULL (state unchanged) if too few pages
+ *                      are free.
+ * attn_pages_free_count — free pages, or NULL for a NULL pool.
+ * attn_pages_table   — for the n sequences seq_ids[0..n-1], in that order,
+ *                      writes seq_lens[i] and the ragged page table of
+ *                      attn_decode_paged (each sequence's pages in logical
+ *                      order, sequences back to back); *table_len receives the
+ *                      number of entries. SEQ for an unknown id; SHAPE (with
+ *                      *table_len set) if table_cap is smaller than needed.
+ *                      Host pointers; copy the arrays to the device for the
+ *                      kernels.
+ */
+typedef struct attn_page_pool attn_page_pool;
+int attn_pages_create(int num_pages, int page_size, attn_page_pool** out);
+void attn_pages_destroy(attn_page_pool* pool);
+int attn_pages_resize(attn_page_pool* pool, int64_t seq_id, int len);
+int attn_pages_free_count(const attn_page_pool* pool);
+int attn_pages_table(const attn_page_pool* pool, const int64_t* seq_ids, int n, int32_t* page_table,
+                     int64_t table_cap, int32_t* seq_lens, int64_t* table_len);
 
 /* attn_strerror — static, never-NULL description of a status code. */
 const char* attn_strerror(int status);

@@ -19,4 +19,5 @@ from .attention import (  # noqa: F401
     gather_sequence,
     decode_paged,
     decode_paged_window,
+    kv_append,
 )

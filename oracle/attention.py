@@ -206,3 +206,24 @@ def decode_paged_window(q, k_pool, v_pool, page_table, seq_lens, page_size, scal
         qb = np.asarray(q[b], dtype=np.float64)[None, :, None, :]
         out[b] = attention(qb, kb, vb, scale, causal=True, window=int(window))[0, :, 0, :]
     return out
+
+
+def kv_append(k_new, v_new, k_pool, v_pool, page_table, seq_lens, page_size):
+    """Pools after appending each sequence's new token, float64 copies.
+
+    "拆开 LLM（二）", section "KV cache": the new token's key and value are
+    appended to the cache before it attends. seq_lens[b] counts that token,
+    so it becomes logical token n-1 (n = seq_lens[b]) of sequence b: slot
+    (n-1) % page_size of physical page page_table[first_b + (n-1) //
+    page_size] ("LLM 核心技术", PagedAttention section), every head at once.
+    """
+    k_out = np.array(k_pool, dtype=np.float64, copy=True)
+    v_out = np.array(v_pool, dtype=np.float64, copy=True)
+    layout = sequence_pages(seq_lens, page_size)
+    for b, n in enumerate(seq_lens):
+        t = int(n) - 1
+        first, _ = layout[b]
+        page = int(page_table[first + t // page_size])
+        k_out[page, :, t % page_size, :] = k_new[b]
+        v_out[page, :, t % page_size, :] = v_new[b]
+    return k_out, v_out

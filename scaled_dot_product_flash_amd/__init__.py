@@ -47,6 +47,19 @@ def load_library():
     lib.attn_decode_paged.restype = i32
     lib.attn_decode_paged_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp]
     lib.attn_decode_paged_window.restype = i32
+    lib.attn_kv_append.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
+    lib.attn_kv_append.restype = i32
+    i64, pp = ctypes.c_int64, ctypes.POINTER(ctypes.c_void_p)
+    lib.attn_pages_create.argtypes = [i32, i32, pp]
+    lib.attn_pages_create.restype = i32
+    lib.attn_pages_destroy.argtypes = [vp]
+    lib.attn_pages_destroy.restype = None
+    lib.attn_pages_resize.argtypes = [vp, i64, i32]
+    lib.attn_pages_resize.restype = i32
+    lib.attn_pages_free_count.argtypes = [vp]
+    lib.attn_pages_free_count.restype = i32
+    lib.attn_pages_table.argtypes = [vp, vp, i32, vp, i64, vp, ctypes.POINTER(ctypes.c_int64)]
+    lib.attn_pages_table.restype = i32
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_release.argtypes = []
@@ -182,3 +195,78 @@ def decode_paged_window(q, k_pool, v_pool, page_table, seq_lens, window, scale=N
                                           int(window), o.data_ptr(), _stream(q))
     _check(rc, "attn_decode_paged_window")
     return o
+
+
+def kv_append(k_new, v_new, k_pool, v_pool, page_table, seq_lens):
+    """Write each sequence's new token (k_new, v_new: [B,Hkv,D] bf16) into its
+    page slot at position seq_lens[b] - 1 (see attn_kv_append)."""
+    import torch
+
+    lib = load_library()
+    _need(k_new, "k_new", torch.bfloat16)
+    _need(v_new, "v_new", torch.bfloat16)
+    _need(k_pool, "k_pool", torch.bfloat16)
+    _need(v_pool, "v_pool", torch.bfloat16)
+    _need(page_table, "page_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    if k_new.dim() != 3 or k_new.shape != v_new.shape or k_pool.dim() != 4 or k_pool.shape != v_pool.shape:
+        raise ValueError("k_new/v_new must be [B,Hkv,D] and the pools [num_pages,Hkv,page_size,D]")
+    B, Hkv, D = k_new.shape
+    if k_pool.shape[1] != Hkv or k_pool.shape[3] != D or seq_lens.shape != (B,):
+        raise ValueError("k_new, the pools and seq_lens do not match")
+    with torch.cuda.device(k_new.device):
+        rc = lib.attn_kv_append(k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                page_table.data_ptr(), seq_lens.data_ptr(), B, Hkv, D, k_pool.shape[2],
+                                _stream(k_new))
+    _check(rc, "attn_kv_append")
+
+
+class PagePool:
+    """Host-side page allocator of a paged KV cache (attn_pages_* in
+    include/attn.h): sequences keyed by int ids own ceil(len / page_size)
+    pages of a global pool; ``table`` writes the ragged page table."""
+
+    def __init__(self, num_pages, page_size):
+        lib = load_library()
+        h = ctypes.c_void_p()
+        _check(lib.attn_pages_create(int(num_pages), int(page_size), ctypes.byref(h)), "attn_pages_create")
+        self._h = h
+        self._lib = lib
+        self.num_pages = int(num_pages)
+        self.page_size = int(page_size)
+
+    def close(self):
+        if self._h:
+            self._lib.attn_pages_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def resize(self, seq_id, length):
+        _check(self._lib.attn_pages_resize(self._h, int(seq_id), int(length)), "attn_pages_resize")
+
+    def free_count(self):
+        n = self._lib.attn_pages_free_count(self._h)
+        _check(min(n, 0), "attn_pages_free_count")
+        return n
+
+    def table(self, seq_ids):
+        """(page_table, seq_lens) as CPU int32 tensors for seq_ids, in order."""
+        import torch
+
+        ids = torch.tensor([int(x) for x in seq_ids], dtype=torch.int64)
+        lens = torch.empty(len(ids), dtype=torch.int32)
+        need = ctypes.c_int64(0)
+        rc = self._lib.attn_pages_table(self._h, ids.data_ptr() if len(ids) else None, len(ids), None, 0,
+                                        lens.data_ptr() if len(ids) else None, ctypes.byref(need))
+        if rc not in (0, -2):  # SHAPE only reports the size needed
+            _check(rc, "attn_pages_table")
+        table = torch.empty(max(need.value, 1), dtype=torch.int32)
+        _check(self._lib.attn_pages_table(self._h, ids.data_ptr() if len(ids) else None, len(ids),
+                                          table.data_ptr(), need.value, lens.data_ptr() if len(ids) else None,
+                                          ctypes.byref(need)), "attn_pages_table")
+        return table[:need.value], lens

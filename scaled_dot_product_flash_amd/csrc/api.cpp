@@ -159,6 +159,22 @@ int attn_decode_paged_window(const void* q, const void* k_pool, const void* v_po
                        stream);
 }
 
+int attn_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool, const int32_t* page_table,
+                   const int32_t* seq_lens, int B, int Hkv, int D, int page_size, hipStream_t stream) {
+    if (B < 0) return ATTN_ERR_SHAPE;
+    if (Hkv < 1) return ATTN_ERR_HEADS;
+    if (D != 64 && D != 128) return ATTN_ERR_HEADDIM;
+    if (page_size < 8 || page_size > 256 || (page_size & (page_size - 1)) != 0) return ATTN_ERR_PAGE;
+    if (B == 0) return ATTN_OK;
+    if (B > 0x7FFFFFFF / 2) return ATTN_ERR_SHAPE;
+    if (!k_new || !v_new || !k_pool || !v_pool || !page_table || !seq_lens) return ATTN_ERR_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool) ||
+        !aligned4(page_table) || !aligned4(seq_lens))
+        return ATTN_ERR_ALIGN;
+    attn::AppendArgs a{k_new, v_new, k_pool, v_pool, page_table, seq_lens, B, Hkv, D, page_size};
+    return hip_status(attn::launch_kv_append(a, stream));
+}
+
 const char* attn_strerror(int status) {
     switch (status) {
         case ATTN_OK: return "success";
@@ -172,6 +188,8 @@ const char* attn_strerror(int status) {
         case ATTN_ERR_ALIGN: return "a tensor pointer is not sufficiently aligned (16 bytes; 4 for int32 tables)";
         case ATTN_ERR_NOMEM: return "device memory for the decode workspace could not be allocated";
         case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+        case ATTN_ERR_FULL: return "the page pool has too few free pages";
+        case ATTN_ERR_SEQ: return "the page pool holds no sequence with this id";
         default: return "unknown attn status code";
     }
 }

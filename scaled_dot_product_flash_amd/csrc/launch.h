@@ -32,6 +32,16 @@ struct DecodeArgs {
     float* ws;      // partial results, decode_workspace_floats() floats
 };
 
+struct AppendArgs {
+    const void* k_new;
+    const void* v_new;
+    void* k_pool;
+    void* v_pool;
+    const int32_t* page_table;
+    const int32_t* seq_lens;
+    int B, Hkv, D, page_size;
+};
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 
@@ -40,5 +50,6 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 int decode_nsplit(int B, int Hq, int Hkv, int num_cu);
 size_t decode_workspace_floats(int B, int Hq, int D, int nsplit);
 hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 
 }  // namespace attn

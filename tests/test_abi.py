@@ -18,6 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
 OK, NULL, SHAPE, HEADS, HEADDIM, MASK, SCALE, PAGE, ALIGN, NOMEM, HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
+FULL, SEQ = -11, -12
 
 
 def _declared():
@@ -40,10 +41,12 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert _declared() == ["attn_decode_paged", "attn_decode_paged_window", "attn_fwd", "attn_fwd_f32",
-                           "attn_release", "attn_strerror"]
+                           "attn_kv_append", "attn_pages_create", "attn_pages_destroy", "attn_pages_free_count",
+                           "attn_pages_resize", "attn_pages_table", "attn_release", "attn_strerror"]
     assert _codes() == {"ATTN_OK": OK, "ATTN_ERR_NULL": NULL, "ATTN_ERR_SHAPE": SHAPE, "ATTN_ERR_HEADS": HEADS,
                         "ATTN_ERR_HEADDIM": HEADDIM, "ATTN_ERR_MASK": MASK, "ATTN_ERR_SCALE": SCALE,
-                        "ATTN_ERR_PAGE": PAGE, "ATTN_ERR_ALIGN": ALIGN, "ATTN_ERR_NOMEM": NOMEM, "ATTN_ERR_HIP": HIP}
+                        "ATTN_ERR_PAGE": PAGE, "ATTN_ERR_ALIGN": ALIGN, "ATTN_ERR_NOMEM": NOMEM, "ATTN_ERR_HIP": HIP,
+                        "ATTN_ERR_FULL": FULL, "ATTN_ERR_SEQ": SEQ}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -156,3 +159,48 @@ def test_ctypes_signature_matches_header(lib):
     assert len(lib.attn_fwd.argtypes) == 14
     assert len(lib.attn_decode_paged.argtypes) == 13
     assert len(lib.attn_decode_paged_window.argtypes) == 14
+
+
+def _app(lib, kn=A, vn=A, kp=A, vp=A, pt=A, sl=A, B=2, Hkv=2, D=128, ps=16):
+    return lib.attn_kv_append(kn, vn, kp, vp, pt, sl, B, Hkv, D, ps, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(kn=None), NULL), (dict(vn=None), NULL), (dict(kp=None), NULL), (dict(vp=None), NULL),
+    (dict(pt=None), NULL), (dict(sl=None), NULL),
+    (dict(B=-1), SHAPE), (dict(Hkv=0), HEADS), (dict(D=96), HEADDIM),
+    (dict(ps=4), PAGE), (dict(ps=24), PAGE), (dict(ps=512), PAGE),
+    (dict(kn=U), ALIGN), (dict(vn=U), ALIGN), (dict(kp=U), ALIGN), (dict(vp=U), ALIGN), (dict(pt=A + 2), ALIGN),
+    (dict(sl=A + 1), ALIGN),
+])
+def test_kv_append_validation(lib, kwargs, code):
+    assert _app(lib, **kwargs) == code
+
+
+def test_kv_append_empty_batch_is_a_no_op(lib):
+    assert _app(lib, kn=None, vn=None, kp=None, vp=None, pt=None, sl=None, B=0) == OK
+
+
+def test_page_pool_argument_errors(lib):
+    h = ctypes.c_void_p()
+    assert lib.attn_pages_create(0, 16, ctypes.byref(h)) == SHAPE
+    assert lib.attn_pages_create(4, 12, ctypes.byref(h)) == PAGE
+    assert lib.attn_pages_create(4, 16, None) == NULL
+    assert lib.attn_pages_resize(None, 1, 3) == NULL
+    assert lib.attn_pages_free_count(None) == NULL
+    n = ctypes.c_int64(0)
+    assert lib.attn_pages_table(None, None, 0, None, 0, None, ctypes.byref(n)) == NULL
+    lib.attn_pages_destroy(None)
+    assert lib.attn_pages_create(4, 16, ctypes.byref(h)) == OK
+    try:
+        assert lib.attn_pages_resize(h, 1, -1) == SHAPE
+        assert lib.attn_pages_resize(h, 1, 4 * 16 + 1) == FULL
+        assert lib.attn_pages_free_count(h) == 4
+        ids = (ctypes.c_int64 * 1)(99)
+        lens = (ctypes.c_int32 * 1)()
+        assert lib.attn_pages_table(h, ids, 1, None, 0, lens, ctypes.byref(n)) == SEQ
+        assert lib.attn_pages_resize(h, 99, 20) == OK
+        assert lib.attn_pages_table(h, ids, 1, None, 0, lens, ctypes.byref(n)) == SHAPE and n.value == 2
+        assert lib.attn_pages_table(h, ids, -1, None, 0, lens, ctypes.byref(n)) == SHAPE
+    finally:
+        lib.attn_pages_destroy(h)

@@ -398,3 +398,51 @@ def test_window_decode_special_cases():
     one = oracle.decode_paged_window(q, kp, vp, table, sl, ps, 0.4, 1)
     for b, n in enumerate(lens):
         np.testing.assert_allclose(one[b], np.broadcast_to(vc[b, 0, n - 1], (Hq, D)), atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# KV append
+
+
+def test_append_then_gather_is_the_longer_cache():
+    rng = np.random.default_rng(15)
+    lens = [1, 8, 9, 30]               # lengths after the append
+    B, Hkv, D, ps = len(lens), 2, 3, 8
+    Smax = max(lens)
+    kc = rng.standard_normal((B, Hkv, Smax, D))
+    vc = rng.standard_normal((B, Hkv, Smax, D))
+    kp, vp, table = _paged_from_contiguous(kc, vc, lens, ps, rng, True)
+    # wipe the last token of each sequence, then append it back
+    kn = np.stack([kc[b, :, n - 1] for b, n in enumerate(lens)])
+    vn = np.stack([vc[b, :, n - 1] for b, n in enumerate(lens)])
+    layout = oracle.sequence_pages(lens, ps)
+    for b, n in enumerate(lens):
+        page = table[layout[b][0] + (n - 1) // ps]
+        kp[page, :, (n - 1) % ps] = 0.0
+        vp[page, :, (n - 1) % ps] = 0.0
+    k2, v2 = oracle.kv_append(kn, vn, kp, vp, table, lens, ps)
+    for b, n in enumerate(lens):
+        np.testing.assert_array_equal(oracle.gather_sequence(k2, table, lens, ps, b), kc[b, :, :n])
+        np.testing.assert_array_equal(oracle.gather_sequence(v2, table, lens, ps, b), vc[b, :, :n])
+    # nothing else moved: only one slot per sequence differs from the input
+    same = (k2 == kp) | (np.isnan(k2) & np.isnan(kp))     # NaN padding compares equal
+    changed = np.argwhere(np.any(~same, axis=(1, 3)))     # (page, slot) pairs
+    assert len(changed) == len(lens)
+
+
+def test_append_and_decode_step_by_step_equals_causal_prefill():
+    # start from an empty cache, append one token per step, decode it
+    rng = np.random.default_rng(16)
+    n, Hq, Hkv, D, ps = 19, 4, 2, 5, 4
+    q = rng.standard_normal((1, Hq, n, D))
+    k = rng.standard_normal((1, Hkv, n, D))
+    v = rng.standard_normal((1, Hkv, n, D))
+    full = oracle.attention(q, k, v, 0.5, causal=True)
+    pages = rng.permutation(8)         # pool of 8 pages handed out in this order
+    kp = np.full((8, Hkv, ps, D), np.nan)
+    vp = np.full((8, Hkv, ps, D), np.nan)
+    for t in range(1, n + 1):
+        table = pages[:(t + ps - 1) // ps].astype(np.int32)
+        kp, vp = oracle.kv_append(k[:, :, t - 1], v[:, :, t - 1], kp, vp, table, [t], ps)
+        step = oracle.decode_paged(q[:, :, t - 1], kp, vp, table, np.array([t]), ps, 0.5)
+        np.testing.assert_allclose(step[0], full[0, :, t - 1], atol=1e-13)
