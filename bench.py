@@ -12,7 +12,8 @@ launch; the decode step's KV GB/s (every cached K/V byte once) is reported
 under ``decode``; ``roofline`` is the prefill kernel against the MI355X dense
 bf16 MFMA peak. ``decode_window`` times the sliding-window decode (window
 4096) on the same cache, outside the timed steps, as KV GB/s over the
-min(len, 4096) most recent tokens of each sequence; ``kv_append`` times the
+min(len, 4096) most recent tokens of each sequence; ``prefill_lse`` times the
+prefill that also returns each row's log-sum-exp; ``kv_append`` times the
 append of one new token per sequence to the same cache. ``cpu_baseline`` times the
 float64 oracle on a bounded sample of the prefill workload on the host cores.
 Progress goes to stderr.
@@ -102,8 +103,9 @@ def cpu_baseline(q, k, v, scale, seconds):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first; the GPU takes ~50 ms of sustained load to reach its steady clocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -176,16 +178,39 @@ def main():
     dwo = torch.empty_like(dq)
     for _ in range(args.warmup):
         attn.decode_paged_window(dq, dkp, dvp, dpt, dsl, WINDOW, scale=d_scale, o=dwo)
-    win_ms = []
-    for _ in range(args.steps):
+    # every timed loop below enqueues back to back and synchronises once, like
+    # the step loop, so the GPU runs under the same sustained load
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in ev:
         attn.fwd(pq, pk, pv, o=po, scale=p_scale, causal=True, window=0)  # same cache state as a step
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        e[0].record()
         attn.decode_paged_window(dq, dkp, dvp, dpt, dsl, WINDOW, scale=d_scale, o=dwo)
-        e1.record()
-        torch.cuda.synchronize()
-        win_ms.append(e0.elapsed_time(e1))
+        e[1].record()
+    torch.cuda.synchronize()
+    win_ms = [e[0].elapsed_time(e[1]) for e in ev]
     assert torch.isfinite(dwo.float()).all()
+
+    # prefill that also writes the per-row log-sum-exp (outside the timed steps)
+    plse = torch.empty((wp["B"], wp["Hq"], wp["Sq"]), dtype=torch.float32, device=dev)
+    lib = attn.load_library()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def fwd_lse():
+        rc = lib.attn_fwd_lse(pq.data_ptr(), pk.data_ptr(), pv.data_ptr(), po.data_ptr(), plse.data_ptr(),
+                              wp["B"], wp["Hq"], wp["Hkv"], wp["Sq"], wp["Sk"], wp["D"], p_scale, 1, 0, stream)
+        assert rc == 0, attn.strerror(rc)
+
+    for _ in range(args.warmup):
+        fwd_lse()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record()
+        fwd_lse()
+        e[1].record()
+        attn.decode_paged(dq, dkp, dvp, dpt, dsl, scale=d_scale, o=do)  # same load as a step
+    torch.cuda.synchronize()
+    lse_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    assert torch.isfinite(plse).all()
 
     # KV append of one new token per sequence (outside the timed steps; it
     # rewrites the last cached token of each sequence)
@@ -193,14 +218,14 @@ def main():
     vn = torch.randn_like(kn)
     for _ in range(args.warmup):
         attn.kv_append(kn, vn, dkp, dvp, dpt, dsl)
-    app_ms = []
-    for _ in range(args.steps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record()
         attn.kv_append(kn, vn, dkp, dvp, dpt, dsl)
-        e1.record()
-        torch.cuda.synchronize()
-        app_ms.append(e0.elapsed_time(e1))
+        e[1].record()
+        attn.decode_paged(dq, dkp, dvp, dpt, dsl, scale=d_scale, o=do)  # the step an append precedes
+    torch.cuda.synchronize()
+    app_ms = [e[0].elapsed_time(e[1]) for e in ev]
 
     import statistics
 
@@ -271,6 +296,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(w_gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(w_gbps / PEAK_HBM_GBPS, 4)},
     }
+    l_mean = statistics.fmean(lse_ms)
+    out["prefill_lse"] = {"ms_mean": round(l_mean, 5), "tflops": round(p_flops / (l_mean * 1e-3) / 1e12, 3),
+                          "frac_peak": round(p_flops / (l_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     a_bytes = 2 * 2 * wd["nseq"] * wd["Hkv"] * wd["D"] * 2   # k_new, v_new read; two slots written
     a_med = statistics.median(app_ms)
     out["kv_append"] = {

@@ -91,6 +91,27 @@ int attn_fwd_f32(const void* q, const void* k, const void* v, void* o,
                  float scale, int causal, int window, hipStream_t stream);
 
 /*
+ * attn_fwd_lse, attn_fwd_f32_lse — attn_fwd / attn_fwd_f32 that also return
+ * the log-sum-exp of each query row, the second output of the FlashAttention
+ * forward in "Attention From Scratch" (FlashAttention module: output and lse),
+ * used to merge attention computed over separate key ranges.
+ *   lse : [B, Hq, Sq] float32, device, 4-byte aligned, caller-owned:
+ *         lse[b,h,i] = ln( sum over the keys j visible to row i of
+ *         exp(scale * q_i . k_j) ), natural logarithm. In the bf16 call the
+ *         sum adds the bf16-rounded probabilities that also weight V (relative
+ *         error below 2^-8 of the sum, so |error| of lse < 2^-8); the f32 call
+ *         keeps float32 throughout. o is identical to the plain call's.
+ *   Errors: those of attn_fwd, and NULL / ALIGN for lse. Empty calls (B == 0
+ *   or Sq == 0) write nothing and accept a NULL lse.
+ */
+int attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                 float scale, int causal, int window, hipStream_t stream);
+int attn_fwd_f32_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                     float scale, int causal, int window, hipStream_t stream);
+
+/*
  * attn_decode_paged — one decode step: each of B sequences has one new query
  * token that attends, without a mask, to every token of its paged KV cache
  * ("拆开 LLM（二）", KV-cache section: the new token's k and v are appended

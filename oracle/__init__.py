@@ -13,6 +13,7 @@ from .attention import (  # noqa: F401
     visible,
     softmax_rows,
     attention,
+    attention_lse,
     attention_rows,
     attention_weights,
     sequence_pages,

@@ -227,3 +227,29 @@ def kv_append(k_new, v_new, k_pool, v_pool, page_table, seq_lens, page_size):
         k_out[page, :, t % page_size, :] = k_new[b]
         v_out[page, :, t % page_size, :] = v_new[b]
     return k_out, v_out
+
+
+def attention_lse(q, k, v, scale, causal=False, window=0, row_chunk=2048):
+    """Log-sum-exp of each row's scaled, masked logits, float64 [B, Hq, Sq].
+
+    lse[b, h, i] = log(sum over visible j of exp(scale * q_i . k_j)), the
+    second output of the FlashAttention forward ("Attention From Scratch",
+    FlashAttention module returning output and lse); softmax weights are
+    exp(S - lse). Computed with the row maximum shifted out first, as in the
+    stable softmax of "拆开 LLM（二）" (section "数值稳定的 softmax").
+    """
+    B, Hq, Sq, _ = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    out = np.empty((B, Hq, Sq), dtype=np.float64)
+    vis = visible(Sq, Sk, causal, window)
+    for b in range(B):
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            kb = np.asarray(k[b, g], dtype=np.float64)
+            for r0 in range(0, Sq, row_chunk):
+                r1 = min(Sq, r0 + row_chunk)
+                qr = np.asarray(q[b, h, r0:r1], dtype=np.float64)
+                s = _scores(qr, kb, scale, vis[r0:r1])
+                m = s.max(axis=1, keepdims=True)
+                out[b, h, r0:r1] = (m + np.log(np.exp(s - m).sum(axis=1, keepdims=True)))[:, 0]
+    return out

@@ -43,6 +43,10 @@ def load_library():
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
         fn.restype = i32
+    for name in ("attn_fwd_lse", "attn_fwd_f32_lse"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
+        fn.restype = i32
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp]
     lib.attn_decode_paged.restype = i32
     lib.attn_decode_paged_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp]
@@ -100,7 +104,7 @@ def _need(t, name, dtype):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _prefill(entry, dtype, q, k, v, o, scale, causal, window):
+def _prefill(entry, dtype, q, k, v, o, scale, causal, window, lse=False):
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -120,11 +124,32 @@ def _prefill(entry, dtype, q, k, v, o, scale, causal, window):
         raise ValueError("all tensors must be on one device")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    if lse:
+        out_lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+        with torch.cuda.device(q.device):
+            rc = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), out_lse.data_ptr(), B, Hq, Hkv,
+                       Sq, Sk, D, float(scale), int(bool(causal)), int(window), _stream(q))
+        _check(rc, entry.__name__)
+        return o, out_lse
     with torch.cuda.device(q.device):
         rc = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, Hq, Hkv, Sq, Sk, D,
                    float(scale), int(bool(causal)), int(window), _stream(q))
     _check(rc, entry.__name__)
     return o
+
+
+def fwd_lse(q, k, v, o=None, scale=None, causal=False, window=0):
+    """fwd plus the float32 log-sum-exp of each row, [B, Hq, Sq]: (o, lse)."""
+    import torch
+
+    return _prefill(load_library().attn_fwd_lse, torch.bfloat16, q, k, v, o, scale, causal, window, lse=True)
+
+
+def fwd_f32_lse(q, k, v, o=None, scale=None, causal=False, window=0):
+    """fwd_f32 plus the float32 log-sum-exp of each row, [B, Hq, Sq]: (o, lse)."""
+    import torch
+
+    return _prefill(load_library().attn_fwd_f32_lse, torch.float32, q, k, v, o, scale, causal, window, lse=True)
 
 
 def fwd(q, k, v, o=None, scale=None, causal=False, window=0):

@@ -94,6 +94,18 @@ int cu_count(int device, int* out) {
     return ATTN_OK;
 }
 
+int prefill_call(bool f32, const void* q, const void* k, const void* v, void* o, float* lse, bool want_lse,
+                 int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale, int causal, int window,
+                 hipStream_t stream) {
+    bool empty = false;
+    const int rc = validate_prefill(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, &empty);
+    if (rc != ATTN_OK || empty) return rc;
+    if (want_lse && !lse) return ATTN_ERR_NULL;
+    if (want_lse && !aligned4(lse)) return ATTN_ERR_ALIGN;
+    attn::PrefillArgs a{q, k, v, o, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, want_lse ? lse : nullptr};
+    return hip_status(f32 ? attn::launch_prefill_f32(a, stream) : attn::launch_prefill_bf16(a, stream));
+}
+
 int decode_call(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
                 const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int page_size, float scale, int window,
                 void* o, hipStream_t stream) {
@@ -130,20 +142,22 @@ extern "C" {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Sq, int Sk,
              int D, float scale, int causal, int window, hipStream_t stream) {
-    bool empty = false;
-    const int rc = validate_prefill(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, &empty);
-    if (rc != ATTN_OK || empty) return rc;
-    attn::PrefillArgs a{q, k, v, o, B, Hq, Hkv, Sq, Sk, D, scale, causal, window};
-    return hip_status(attn::launch_prefill_bf16(a, stream));
+    return prefill_call(false, q, k, v, o, nullptr, false, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, stream);
 }
 
 int attn_fwd_f32(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Sq,
                  int Sk, int D, float scale, int causal, int window, hipStream_t stream) {
-    bool empty = false;
-    const int rc = validate_prefill(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, &empty);
-    if (rc != ATTN_OK || empty) return rc;
-    attn::PrefillArgs a{q, k, v, o, B, Hq, Hkv, Sq, Sk, D, scale, causal, window};
-    return hip_status(attn::launch_prefill_f32(a, stream));
+    return prefill_call(true, q, k, v, o, nullptr, false, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, stream);
+}
+
+int attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                 int Sq, int Sk, int D, float scale, int causal, int window, hipStream_t stream) {
+    return prefill_call(false, q, k, v, o, lse, true, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, stream);
+}
+
+int attn_fwd_f32_lse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                     int Sq, int Sk, int D, float scale, int causal, int window, hipStream_t stream) {
+    return prefill_call(true, q, k, v, o, lse, true, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, stream);
 }
 
 int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,

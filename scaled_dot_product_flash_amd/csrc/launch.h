@@ -16,6 +16,7 @@ struct PrefillArgs {
     int B, Hq, Hkv, Sq, Sk, D;
     float scale;
     int causal, window;
+    float* lse;     // [B, Hq, Sq] float32 log-sum-exp per row, or nullptr
 };
 
 struct DecodeArgs {

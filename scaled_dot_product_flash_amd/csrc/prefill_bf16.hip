@@ -74,7 +74,7 @@ constexpr float kLazy = 8.0f;
 template <int D, bool NEG>
 __global__ __launch_bounds__(kThreads, 2)
 void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                         const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                         const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
                          int Hq, int Hkv, int Sq, int Sk, float c2, int causal, int window,
                          int nqt, int nitems, int per_xcd) {
     constexpr int BN = Tile<D>::BN;
@@ -328,6 +328,10 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     if (!wave_rows || qrow >= Sq) return;
     const float l_tot = l_run + xor32(l_run);
     const float inv = 1.f / l_tot;
+    // log-sum-exp of the scaled logits, natural log: sum_j exp(scale s_j)
+    // = 2^m_ref * l with m_ref the reference maximum in log2 units
+    if (LSE != nullptr && hh == 0)
+        LSE[((size_t)b * Hq + h) * Sq + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
     uint16_t* op = O + qo_base + (size_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -373,7 +377,7 @@ __device__ __forceinline__ float2 halves(float x) {
 template <int NW, bool NEG>
 __global__ __launch_bounds__(64 * NW, 2)
 void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                         const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                         const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
                          int Hq, int Hkv, int Sq, int Sk, float c2, int causal, int window,
                          int nqt, int nitems, int per_xcd) {
     constexpr int D = 128, BN = 64, KB = 2, KS = 4, DS = 8, DB = 4, CPR = 16;
@@ -723,6 +727,10 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     if (qrow >= Sq) return;
     const float2 lh = halves(l_run);
     const float inv = 1.f / (lh.x + lh.y);
+    // log-sum-exp of the scaled logits, natural log: sum_j exp(scale s_j)
+    // = 2^m_ref * l with m_ref the reference maximum in log2 units
+    if (LSE != nullptr && hh == 0)
+        LSE[((size_t)b * Hq + h) * Sq + qrow] = (m_run + __log2f(lh.x + lh.y)) * 0.69314718055994531f;
     uint16_t* op = O + qo_base + (size_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -747,7 +755,7 @@ hipError_t launch_pipe(const PrefillArgs& a, hipStream_t stream) {
     float c2 = a.scale * 1.4426950408889634f;
     if (c2 == 0.f) c2 = 1e-30f;
     hipLaunchKernelGGL((prefill_pipe_kernel<NW, NEG>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                        a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)per_xcd);
     return hipGetLastError();
 }
@@ -764,7 +772,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     // exp2(0) = 1 for finite logits) and keeps masked logits at -inf
     if (c2 == 0.f) c2 = 1e-30f;
     hipLaunchKernelGGL((prefill_bf16_kernel<D, NEG>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                        a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)per_xcd);
     return hipGetLastError();
 }

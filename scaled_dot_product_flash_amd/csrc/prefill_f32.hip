@@ -27,7 +27,7 @@ constexpr int kBN = 32;
 template <int D>
 __global__ __launch_bounds__(kThreads)
 void prefill_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
-                        const float* __restrict__ V, float* __restrict__ O,
+                        const float* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
                         int Hq, int Hkv, int Sq, int Sk, float c2, int causal, int window, int nqt) {
     constexpr int DP = D / 4;  // dims per lane
     __shared__ float ks[kBN][D];
@@ -107,6 +107,9 @@ void prefill_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K
 
     if (!row_ok) return;
     const float inv = 1.f / l_run;
+    // log-sum-exp of the scaled logits, natural log (m_run in log2 units)
+    if (LSE != nullptr && part == 0)
+        LSE[((size_t)b * Hq + h) * Sq + row] = (m_run + log2f(l_run)) * 0.69314718055994531f;
 #pragma unroll
     for (int x = 0; x < DP; ++x) O[qo_base + (size_t)row * D + part + 4 * x] = o[x] * inv;
 }
@@ -118,7 +121,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     const float c2 = a.scale * 1.4426950408889634f;
     hipLaunchKernelGGL((prefill_f32_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
                        a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt);
     return hipGetLastError();
 }

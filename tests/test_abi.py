@@ -41,7 +41,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert _declared() == ["attn_decode_paged", "attn_decode_paged_window", "attn_fwd", "attn_fwd_f32",
-                           "attn_kv_append", "attn_pages_create", "attn_pages_destroy", "attn_pages_free_count",
+                           "attn_fwd_f32_lse", "attn_fwd_lse", "attn_kv_append", "attn_pages_create", "attn_pages_destroy", "attn_pages_free_count",
                            "attn_pages_resize", "attn_pages_table", "attn_release", "attn_strerror"]
     assert _codes() == {"ATTN_OK": OK, "ATTN_ERR_NULL": NULL, "ATTN_ERR_SHAPE": SHAPE, "ATTN_ERR_HEADS": HEADS,
                         "ATTN_ERR_HEADDIM": HEADDIM, "ATTN_ERR_MASK": MASK, "ATTN_ERR_SCALE": SCALE,
@@ -159,6 +159,7 @@ def test_ctypes_signature_matches_header(lib):
     assert len(lib.attn_fwd.argtypes) == 14
     assert len(lib.attn_decode_paged.argtypes) == 13
     assert len(lib.attn_decode_paged_window.argtypes) == 14
+    assert len(lib.attn_fwd_lse.argtypes) == len(lib.attn_fwd_f32_lse.argtypes) == 15
 
 
 def _app(lib, kn=A, vn=A, kp=A, vp=A, pt=A, sl=A, B=2, Hkv=2, D=128, ps=16):
@@ -204,3 +205,24 @@ def test_page_pool_argument_errors(lib):
         assert lib.attn_pages_table(h, ids, -1, None, 0, lens, ctypes.byref(n)) == SHAPE
     finally:
         lib.attn_pages_destroy(h)
+
+
+def _fwd_lse(lib, lse=A, f32=False, **kw):
+    args = dict(q=A, k=A, v=A, o=A, B=1, Hq=4, Hkv=2, Sq=8, Sk=8, D=64, scale=0.125, causal=1, window=0)
+    args.update(kw)
+    fn = lib.attn_fwd_f32_lse if f32 else lib.attn_fwd_lse
+    return fn(args["q"], args["k"], args["v"], args["o"], lse, args["B"], args["Hq"], args["Hkv"], args["Sq"],
+              args["Sk"], args["D"], args["scale"], args["causal"], args["window"], None)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_fwd_lse_validation(lib, f32):
+    assert _fwd_lse(lib, lse=None, f32=f32) == NULL
+    assert _fwd_lse(lib, lse=A + 2, f32=f32) == ALIGN
+    # the arguments shared with attn_fwd are checked the same way, first
+    assert _fwd_lse(lib, f32=f32, D=96) == HEADDIM
+    assert _fwd_lse(lib, f32=f32, causal=0, window=3) == MASK
+    assert _fwd_lse(lib, f32=f32, q=None) == NULL
+    # empty calls need no pointer at all
+    assert _fwd_lse(lib, lse=None, f32=f32, q=None, k=None, v=None, o=None, B=0) == OK
+    assert _fwd_lse(lib, lse=None, f32=f32, q=None, k=None, v=None, o=None, Sq=0) == OK

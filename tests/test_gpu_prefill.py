@@ -217,3 +217,73 @@ def test_o_is_not_written_outside_its_rows():
     attn.fwd(qd, kd, vd, o=o, causal=True)
     torch.cuda.synchronize()
     assert torch.all(big[2 * 70 * 64:] == 7.0)
+
+
+# ---- log-sum-exp output ----------------------------------------------------------
+# bf16 path: the row sum adds the bf16-rounded probabilities, each within 2^-9
+# (relative) of the exact one, so |error of lse| <= -log(1 - 2^-9) < 2^-8;
+# f32 path: float32 logits and sums, bar 1e-5 on the natural-log value.
+LSE_BF16_BAR = 2.0 ** -8
+LSE_F32_BAR = 1e-5
+
+LSE_SHAPES = [
+    (1, 1, 1, 1, 1, 64, False, 0),
+    (2, 4, 2, 77, 77, 128, True, 0),
+    (1, 8, 1, 129, 129, 128, True, 0),
+    (1, 8, 8, 200, 333, 64, False, 0),
+    (1, 4, 2, 100, 300, 128, True, 0),
+    (3, 6, 3, 257, 257, 64, True, 7),
+    (1, 2, 1, 500, 700, 128, True, 100),
+    (2, 16, 4, 1000, 1000, 128, True, 0),
+]
+
+
+@pytest.mark.parametrize("shape", LSE_SHAPES)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_lse_output(shape, dtype):
+    B, Hq, Hkv, Sq, Sk, D, causal, window = shape
+    say(f"lse {dtype} {shape}")
+    q, k, v = inputs.prefill_inputs(B, Hq, Hkv, Sq, Sk, D, dtype, seed=sum(shape[:6]) + 5)
+    scale = 1.0 / math.sqrt(D)
+    qd, kd, vd = cuda(q, k, v)
+    fn = attn.fwd_f32_lse if dtype == "f32" else attn.fwd_lse
+    o, lse = fn(qd, kd, vd, scale=scale, causal=causal, window=window)
+    plain = (attn.fwd_f32 if dtype == "f32" else attn.fwd)(qd, kd, vd, scale=scale, causal=causal, window=window)
+    torch.cuda.synchronize()
+    assert torch.equal(o, plain)            # the extra output changes nothing else
+    want = oracle.attention_lse(f64(q), f64(k), f64(v), scale, causal, window)
+    err = np.abs(f64(lse.cpu()) - want)
+    bar = LSE_F32_BAR if dtype == "f32" else LSE_BF16_BAR
+    assert err.max() <= bar, (err.max(), bar)
+
+
+def test_lse_full_size_workload_sampled_rows():
+    w = inputs.WORKLOADS["gqa_causal_4k"]
+    say("lse workload gqa_causal_4k")
+    q, k, v = inputs.workload_inputs("gqa_causal_4k")
+    scale = 1.0 / math.sqrt(w["D"])
+    o, lse = attn.fwd_lse(*cuda(q, k, v), scale=scale, causal=True)
+    lse = lse.cpu()
+    qn, kn, vn = (t.float().numpy() for t in (q, k, v))
+    for b, h in [(0, 0), (3, 31), (2, 5)]:
+        rows = [0, 1, 127, 128, 2048, 4095]
+        s = (qn[b, h, rows].astype(np.float64) @ kn[b, h // 4].T.astype(np.float64)) * scale
+        vis = oracle.visible(4096, 4096, True, 0)[rows]
+        s = np.where(vis, s, -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        want = (m + np.log(np.exp(s - m).sum(axis=1, keepdims=True)))[:, 0]
+        assert np.abs(f64(lse[b, h, rows]) - want).max() <= LSE_BF16_BAR
+
+
+def test_lse_merges_two_key_halves():
+    # the use of lse: attention over keys [0, n) equals the lse-weighted merge
+    # of attention over [0, n/2) and [n/2, n) (non-causal halves)
+    q, k, v = inputs.prefill_inputs(1, 4, 2, 64, 512, 128, "f32", 44)
+    qd, kd, vd = cuda(q, k, v)
+    o, _ = attn.fwd_f32_lse(qd, kd, vd)
+    o1, l1 = attn.fwd_f32_lse(qd, kd[:, :, :256].contiguous(), vd[:, :, :256].contiguous())
+    o2, l2 = attn.fwd_f32_lse(qd, kd[:, :, 256:].contiguous(), vd[:, :, 256:].contiguous())
+    lm = torch.logaddexp(l1, l2)
+    merged = o1 * torch.exp(l1 - lm)[..., None] + o2 * torch.exp(l2 - lm)[..., None]
+    torch.cuda.synchronize()
+    assert (merged - o).abs().max().item() <= 1e-5

@@ -446,3 +446,56 @@ def test_append_and_decode_step_by_step_equals_causal_prefill():
         kp, vp = oracle.kv_append(k[:, :, t - 1], v[:, :, t - 1], kp, vp, table, [t], ps)
         step = oracle.decode_paged(q[:, :, t - 1], kp, vp, table, np.array([t]), ps, 0.5)
         np.testing.assert_allclose(step[0], full[0, :, t - 1], atol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# log-sum-exp
+
+
+def _brute_lse(q, k, scale, causal, window):
+    B, Hq, Sq = len(q), len(q[0]), len(q[0][0])
+    Hkv, Sk, D = len(k[0]), len(k[0][0]), len(k[0][0][0])
+    out = np.zeros((B, Hq, Sq))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            for i in range(Sq):
+                t = i + (Sk - Sq) + 1
+                first = max(0, t - window) if window else 0
+                keys = list(range(first, t)) if causal else list(range(Sk))
+                out[b, h, i] = math.log(math.fsum(
+                    math.exp(math.fsum(q[b][h][i][c] * k[b][g][j][c] for c in range(D)) * scale) for j in keys))
+    return out
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_lse_brute_force(case):
+    B, Hq, Hkv, Sq, Sk, D, causal, window = case
+    rng = np.random.default_rng(sum(case[:6]))
+    q = rng.standard_normal((B, Hq, Sq, D))
+    k = rng.standard_normal((B, Hkv, Sk, D))
+    v = rng.standard_normal((B, Hkv, Sk, D))
+    got = oracle.attention_lse(q, k, v, 0.7, causal, window)
+    np.testing.assert_allclose(got, _brute_lse(q.tolist(), k.tolist(), 0.7, causal, window), atol=1e-12)
+
+
+def test_lse_closed_forms():
+    rng = np.random.default_rng(17)
+    S, D = 9, 4
+    k = rng.standard_normal((1, 1, S, D))
+    v = rng.standard_normal((1, 1, S, D))
+    # Q = 0: every visible logit is 0, lse = log(number of visible keys)
+    lse = oracle.attention_lse(np.zeros((1, 1, S, D)), k, v, 1.0, causal=True, window=4)
+    np.testing.assert_allclose(lse[0, 0], np.log([min(i + 1, 4) for i in range(S)]), atol=1e-15)
+    # softmax weights are exp(S - lse): rows of the weight matrix
+    q = rng.standard_normal((1, 1, S, D))
+    w = oracle.attention_weights(q[0, 0], k[0, 0], 0.3, causal=True)
+    lse = oracle.attention_lse(q, k, v, 0.3, causal=True)[0, 0]
+    s = q[0, 0] @ k[0, 0].T * 0.3
+    vis = oracle.visible(S, S, True, 0)
+    np.testing.assert_allclose(np.where(vis, np.exp(s - lse[:, None]), 0.0), w, atol=1e-14)
+    # huge logits do not overflow: two keys with logits 1000 and 1000 - d
+    q2 = np.array([[[[1000.0]]]])
+    k2 = np.array([[[[1.0], [0.99]]]])
+    lse2 = oracle.attention_lse(q2, k2, k2, 1.0)
+    np.testing.assert_allclose(lse2[0, 0, 0], 1000.0 + math.log1p(math.exp(-10.0)), rtol=0, atol=1e-12)
