@@ -558,14 +558,19 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
 
     // One pipeline step: P(t) from scur, O += P(t)·V(t) from vb and, if NEXT,
     // S(t+1) from kb into snew; returns the extreme of the unmasked S(t+1).
+    // K operands of the first chunk (S-steps 0 and 1 of block 1), read by the
+    // caller ahead of the step's DMA issue so their LDS latency overlaps it
+    auto kfirst = [&](const unsigned char* kb, bf16x8 (&kr)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) kr[i] = kread(kb, i, 1);
+    };
     auto main_block = [&](auto next_c, const unsigned char* kb, const unsigned char* vb,
-                          f32x16 (&scur)[KB], f32x16 (&snew)[KB]) __attribute__((always_inline)) {
+                          f32x16 (&scur)[KB], f32x16 (&snew)[KB], bf16x8 (&kr)[4]) __attribute__((always_inline)) {
         constexpr bool NEXT = decltype(next_c)::value;
         apply_rescale();
         const float msub = (m_run == -INFINITY) ? 0.f : m_run;
         float la = l_run, lb = 0.f;
         bf16x8 pb[KS];
-        bf16x8 kr[4];
         bf16x8 vr[2][2];
         float mx = masked;
         // Ten chunks. Chunk c < 8: the two MFMAs of S(t+1) for block 1 - c/4,
@@ -581,10 +586,6 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             dst[0] = vop(vb, ks, db0);
             dst[1] = vop(vb, ks, db0 + 1);
         };
-        if constexpr (NEXT) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) kr[i] = kread(kb, kst(0, i), kblk(0));
-        }
 #pragma unroll
         for (int c = 0; c < 10; ++c) {
             __builtin_amdgcn_sched_barrier(0);
@@ -653,9 +654,11 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     using F = std::integral_constant<bool, false>;
     auto step = [&](int t, const unsigned char* kb, const unsigned char* vb, unsigned char* kdst,
                     unsigned char* vdst, f32x16 (&scur)[KB], f32x16 (&snew)[KB]) __attribute__((always_inline)) {
+        bf16x8 kr[4];
+        kfirst(kb, kr);
         if (t + 2 < t_end) issue(krs, t + 2, kdst, false);
         issue(vrs, t + 1, vdst, true);
-        float mx = main_block(T{}, kb, vb, scur, snew);
+        float mx = main_block(T{}, kb, vb, scur, snew, kr);
         if (is_edge(t + 1)) mx = edge_extreme(snew, (t + 1) * BN);
         settle(mx);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -666,7 +669,8 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                          f32x16 (&scur)[KB]) __attribute__((always_inline)) {
         if (u + 2 < t_end) issue(krs, u + 2, kdst, false);
         if (u + 1 < t_end) issue(vrs, u + 1, vdst, true);
-        main_block(F{}, k_lds0, vb, scur, scur);
+        bf16x8 kr[4];
+        main_block(F{}, k_lds0, vb, scur, scur, kr);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     };
