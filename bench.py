@@ -13,7 +13,9 @@ under ``decode``; ``roofline`` is the prefill kernel against the MI355X dense
 bf16 MFMA peak. ``decode_window`` times the sliding-window decode (window
 4096) on the same cache, outside the timed steps, as KV GB/s over the
 min(len, 4096) most recent tokens of each sequence; ``prefill_lse`` times the
-prefill that also returns each row's log-sum-exp; ``kv_append`` times the
+prefill that also returns each row's log-sum-exp; ``prefill_paged`` times a
+chunked prefill (512 new tokens per sequence) against a paged cache;
+``kv_append`` times the
 append of one new token per sequence to the same cache. ``cpu_baseline`` times the
 float64 oracle on a bounded sample of the prefill workload on the host cores.
 Progress goes to stderr.
@@ -212,6 +214,24 @@ def main():
     lse_ms = [e[0].elapsed_time(e[1]) for e in ev]
     assert torch.isfinite(plse).all()
 
+    # chunked prefill against a paged cache (outside the timed steps)
+    wc = inputs.WORKLOADS["chunked_prefill_paged"]
+    cd = inputs.workload_inputs("chunked_prefill_paged")
+    cq, ckp, cvp, cpt, csl = (cd[n].to(dev) for n in ("q", "k_pool", "v_pool", "page_table", "seq_lens"))
+    co = torch.empty_like(cq)
+    for _ in range(args.warmup):
+        attn.fwd_paged(cq, ckp, cvp, cpt, csl, o=co, causal=True)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record()
+        attn.fwd_paged(cq, ckp, cvp, cpt, csl, o=co, causal=True)
+        e[1].record()
+    torch.cuda.synchronize()
+    chunk_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    assert torch.isfinite(co.float()).all()
+    chunk_flops = sum(work.attention_flops(work.visible_pairs(wc["Sq"], int(n), True, 0), wc["D"]) * wc["Hq"]
+                      for n in cd["seq_lens"].tolist())
+
     # KV append of one new token per sequence (outside the timed steps; it
     # rewrites the last cached token of each sequence)
     kn = torch.randn((wd["nseq"], wd["Hkv"], wd["D"]), device=dev).to(torch.bfloat16)
@@ -299,6 +319,14 @@ def main():
     l_mean = statistics.fmean(lse_ms)
     out["prefill_lse"] = {"ms_mean": round(l_mean, 5), "tflops": round(p_flops / (l_mean * 1e-3) / 1e12, 3),
                           "frac_peak": round(p_flops / (l_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    c_mean = statistics.fmean(chunk_ms)
+    out["prefill_paged"] = {
+        "workload": f"chunked prefill: {wc['nseq']} seqs, {wc['Sq']} new tokens each, cache "
+                    f"{wc['len_lo']}..{wc['len_hi']} tokens, Hq={wc['Hq']} Hkv={wc['Hkv']} D={wc['D']} "
+                    f"page_size={wc['page_size']}, causal",
+        "flop_per_call": chunk_flops, "ms_mean": round(c_mean, 5),
+        "tflops": round(chunk_flops / (c_mean * 1e-3) / 1e12, 3),
+        "frac_peak": round(chunk_flops / (c_mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     a_bytes = 2 * 2 * wd["nseq"] * wd["Hkv"] * wd["D"] * 2   # k_new, v_new read; two slots written
     a_med = statistics.median(app_ms)
     out["kv_append"] = {

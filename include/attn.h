@@ -112,6 +112,32 @@ int attn_fwd_f32_lse(const void* q, const void* k, const void* v, void* o, float
                      float scale, int causal, int window, hipStream_t stream);
 
 /*
+ * attn_fwd_paged — prefill of Sq new tokens per sequence against a paged KV
+ * cache (chunked prefill): the prefill of attn_fwd with K and V read through
+ * the page table of attn_decode_paged instead of from contiguous tensors
+ * ("LLM 核心技术", PagedAttention section: attention reads the cache through
+ * the page table; "拆开 LLM（二）", KV-cache section: new tokens attend to the
+ * cached ones).
+ *   q, o        : [B, Hq, Sq, D] bfloat16, the Sq newest tokens of each
+ *                 sequence, whose k and v are already in the cache.
+ *   k_pool, v_pool, page_table, seq_lens, page_size : as in
+ *                 attn_decode_paged; sequence b has Sk_b = seq_lens[b] cached
+ *                 tokens and query row i sits at position Sk_b - Sq + i
+ *                 (bottom-right alignment, as in attn_fwd with Sq <= Sk).
+ *   lse         : NULL, or [B, Hq, Sq] float32 receiving the log-sum-exp of
+ *                 each row as in attn_fwd_lse.
+ *   D must be 128 (ATTN_ERR_HEADDIM otherwise). causal / window as in
+ *   attn_fwd. Device-side preconditions: those of attn_decode_paged, and
+ *   seq_lens[b] >= Sq when causal. Slots at or past seq_lens[b] are never
+ *   used (they may hold NaN). Errors: those of attn_fwd and attn_decode_paged
+ *   for the same arguments; B == 0 or Sq == 0 is a no-op.
+ */
+int attn_fwd_paged(const void* q, const void* k_pool, const void* v_pool,
+                   const int32_t* page_table, const int32_t* seq_lens, void* o, float* lse,
+                   int B, int Hq, int Hkv, int Sq, int D, int page_size,
+                   float scale, int causal, int window, hipStream_t stream);
+
+/*
  * attn_decode_paged — one decode step: each of B sequences has one new query
  * token that attends, without a mask, to every token of its paged KV cache
  * ("拆开 LLM（二）", KV-cache section: the new token's k and v are appended

@@ -21,4 +21,5 @@ from .attention import (  # noqa: F401
     decode_paged,
     decode_paged_window,
     kv_append,
+    prefill_paged,
 )

@@ -253,3 +253,21 @@ def attention_lse(q, k, v, scale, causal=False, window=0, row_chunk=2048):
                 m = s.max(axis=1, keepdims=True)
                 out[b, h, r0:r1] = (m + np.log(np.exp(s - m).sum(axis=1, keepdims=True)))[:, 0]
     return out
+
+
+def prefill_paged(q, k_pool, v_pool, page_table, seq_lens, page_size, scale, causal=False, window=0):
+    """Attention of the Sq newest tokens of each sequence over its paged
+    cache, float64 [B, Hq, Sq, D].
+
+    q: [B, Hq, Sq, D]; the cache of sequence b holds n = seq_lens[b] tokens
+    (the Sq new ones included) in pages of a pool ("LLM 核心技术",
+    PagedAttention section). The gathered cache is attended as in
+    `attention`, query row i at position n - Sq + i (bottom-right).
+    """
+    B, Hq, Sq, D = q.shape
+    out = np.empty((B, Hq, Sq, v_pool.shape[3]), dtype=np.float64)
+    for b in range(B):
+        kb = gather_sequence(k_pool, page_table, seq_lens, page_size, b)[None]
+        vb = gather_sequence(v_pool, page_table, seq_lens, page_size, b)[None]
+        out[b] = attention(np.asarray(q[b:b + 1], dtype=np.float64), kb, vb, scale, causal, window)[0]
+    return out

@@ -51,6 +51,8 @@ def load_library():
     lib.attn_decode_paged.restype = i32
     lib.attn_decode_paged_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp]
     lib.attn_decode_paged_window.restype = i32
+    lib.attn_fwd_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
+    lib.attn_fwd_paged.restype = i32
     lib.attn_kv_append.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
     lib.attn_kv_append.restype = i32
     i64, pp = ctypes.c_int64, ctypes.POINTER(ctypes.c_void_p)
@@ -295,3 +297,36 @@ class PagePool:
                                           table.data_ptr(), need.value, lens.data_ptr() if len(ids) else None,
                                           ctypes.byref(need)), "attn_pages_table")
         return table[:need.value], lens
+
+
+def fwd_paged(q, k_pool, v_pool, page_table, seq_lens, o=None, scale=None, causal=False, window=0, lse=False):
+    """Prefill of q [B,Hq,Sq,D] (the newest Sq tokens of each sequence) against
+    a paged cache (see attn_fwd_paged); returns o, or (o, lse) with lse=True."""
+    import torch
+
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    _need(k_pool, "k_pool", torch.bfloat16)
+    _need(v_pool, "v_pool", torch.bfloat16)
+    _need(page_table, "page_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    if q.dim() != 4 or k_pool.dim() != 4 or k_pool.shape != v_pool.shape:
+        raise ValueError("q must be [B,Hq,Sq,D] and the pools [num_pages,Hkv,page_size,D]")
+    B, Hq, Sq, D = q.shape
+    Hkv, ps = k_pool.shape[1], k_pool.shape[2]
+    if k_pool.shape[3] != D or seq_lens.shape != (B,):
+        raise ValueError("pool head dim or seq_lens length does not match q")
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", torch.bfloat16)
+    if o.shape != q.shape:
+        raise ValueError("o must have the shape of q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out_lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if lse else None
+    with torch.cuda.device(q.device):
+        rc = lib.attn_fwd_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(),
+                                seq_lens.data_ptr(), o.data_ptr(), out_lse.data_ptr() if lse else None, B, Hq, Hkv,
+                                Sq, D, ps, float(scale), int(bool(causal)), int(window), _stream(q))
+    _check(rc, "attn_fwd_paged")
+    return (o, out_lse) if lse else o

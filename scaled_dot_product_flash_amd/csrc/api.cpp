@@ -160,6 +160,29 @@ int attn_fwd_f32_lse(const void* q, const void* k, const void* v, void* o, float
     return prefill_call(true, q, k, v, o, lse, true, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, stream);
 }
 
+int attn_fwd_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                   const int32_t* seq_lens, void* o, float* lse, int B, int Hq, int Hkv, int Sq, int D,
+                   int page_size, float scale, int causal, int window, hipStream_t stream) {
+    if (B < 0 || Sq < 0) return ATTN_ERR_SHAPE;
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_HEADS;
+    if (D != 128) return ATTN_ERR_HEADDIM;
+    if (page_size < 8 || page_size > 256 || (page_size & (page_size - 1)) != 0) return ATTN_ERR_PAGE;
+    if (causal != 0 && causal != 1) return ATTN_ERR_MASK;
+    if (window < 0 || (window > 0 && !causal)) return ATTN_ERR_MASK;
+    if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+    if (B == 0 || Sq == 0) return ATTN_OK;
+    if (!product_fits(B, Hq, Sq, D)) return ATTN_ERR_SHAPE;
+    const long long items = (long long)B * Hq * ((Sq + 63) / 64) + 8;
+    if (items > 0x7FFFFFFFLL) return ATTN_ERR_SHAPE;
+    if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !o) return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o) || !aligned4(page_table) ||
+        !aligned4(seq_lens) || (lse && !aligned4(lse)))
+        return ATTN_ERR_ALIGN;
+    attn::PrefillArgs a{q, k_pool, v_pool, o, B, Hq, Hkv, Sq, 0, D, scale, causal, window, lse,
+                        page_table, seq_lens, page_size};
+    return hip_status(attn::launch_prefill_bf16(a, stream));
+}
+
 int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
                       const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int page_size, float scale,
                       void* o, hipStream_t stream) {

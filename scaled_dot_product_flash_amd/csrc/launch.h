@@ -17,6 +17,11 @@ struct PrefillArgs {
     float scale;
     int causal, window;
     float* lse;     // [B, Hq, Sq] float32 log-sum-exp per row, or nullptr
+    // paged K/V (k, v are then [pages, Hkv, page_size, D] pools and Sk is
+    // per sequence); nullptr page_table: contiguous [B, Hkv, Sk, D]
+    const int32_t* page_table = nullptr;
+    const int32_t* seq_lens = nullptr;
+    int page_size = 0;
 };
 
 struct DecodeArgs {

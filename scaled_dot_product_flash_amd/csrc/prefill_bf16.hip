@@ -374,12 +374,16 @@ __device__ __forceinline__ float2 halves(float x) {
     return make_float2(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
 
-template <int NW, bool NEG>
+// PAGED: K and V come from a paged cache ([pages, Hkv, ps, D] pools, a
+// ragged page table and per-sequence lengths, the layout of the paged decode)
+// instead of [B, Hkv, Sk, D] slices; Sk is then the sequence's length.
+template <int NW, bool NEG, bool PAGED>
 __global__ __launch_bounds__(64 * NW, 2)
 void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
                          int Hq, int Hkv, int Sq, int Sk, float c2, int causal, int window,
-                         int nqt, int nitems, int per_xcd) {
+                         int nqt, int nitems, int per_xcd,
+                         const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int ps_log2) {
     constexpr int D = 128, BN = 64, KB = 2, KS = 4, DS = 8, DB = 4, CPR = 16;
     constexpr int TILE_BYTES = BN * D * 2;
     constexpr int SLOTS = TILE_BYTES / 1024;
@@ -400,7 +404,7 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     const int qt = nqt - 1 - (r1 % nqt);
     const int bg = r1 / nqt;
     const int g = bg % Hkv;
-    const int b = bg / Hkv;
+    int b = bg / Hkv;
     const int h = g * G + hg;
 
     const int tid = threadIdx.x;
@@ -409,13 +413,48 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     const int ln = lane & 31;
     const int hh = lane >> 5;
 
+    // paged: the sequence's length and its first page-table entry
+    // off_b = sum over j < b of ceil(lens[j] / page_size)
+    int off_b = 0;
+    if constexpr (PAGED) {
+        // sequence slot b of the grid takes the sequence of b-th largest length
+        // (ties by index; up to 64 * NW sequences), so the longest caches,
+        // the most work, are dispatched first
+        const int B = nitems / (Hq * nqt);
+        if (B <= 64 * NW) {
+            __shared__ int sh_seq;
+            if (tid < B) {
+                const int my = lens[tid];
+                int rank = 0;
+                for (int j = 0; j < B; ++j) {
+                    const int lj = lens[j];
+                    rank += (lj > my) || (lj == my && j < tid);
+                }
+                if (rank == b) sh_seq = tid;
+            }
+            __syncthreads();
+            b = sh_seq;
+        }
+        __shared__ int sh_part[NW];
+        int part = 0;
+        for (int j = tid; j < b; j += 64 * NW) part += (lens[j] + (1 << ps_log2) - 1) >> ps_log2;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
+        if (lane == 0) sh_part[wave] = part;
+        __syncthreads();
+#pragma unroll
+        for (int x = 0; x < NW; ++x) off_b += sh_part[x];
+        Sk = lens[b];
+        if (Sk < 1) return;   // outside the precondition seq_lens[b] >= 1: nothing to do
+    }
+
     const int off = Sk - Sq;
     const int i0 = qt * BMW;
     const int row_end = min(i0 + BMW, Sq);
 
     const size_t qo_base = ((size_t)b * Hq + h) * (size_t)Sq * D;
-    const size_t kv_base = ((size_t)b * Hkv + g) * (size_t)Sk * D;
-    const int kv_bytes = Sk * D * 2;
+    const size_t kv_base = PAGED ? 0 : ((size_t)b * Hkv + g) * (size_t)Sk * D;
+    const int kv_bytes = PAGED ? 0 : Sk * D * 2;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(K + kv_base), 0, kv_bytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(V + kv_base), 0, kv_bytes, kRsrcWord3);
 
@@ -465,16 +504,36 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     static_assert(SLOTS / NW >= 1, "DMA slots");
     const unsigned kv_lane_k = (unsigned)((dma_row * D + 8 * ((lane & 15) ^ (dma_row & 15))) * 2);
     const unsigned kv_lane_v = (unsigned)((dma_row * D + 8 * ((lane & 15) ^ ((dma_row & 3) << 2))) * 2);
+    // paged: the four rows of a slot start at a multiple of 4 and so lie in
+    // one page (page_size >= 8); the slot gets a buffer resource over that
+    // (page, kv head) tile, and rows at or past Sk (or a slot wholly past it,
+    // whose page is not even looked up) read zeros through the range check
+    const int ps = 1 << ps_log2;
+    const unsigned pg_lane_k = (unsigned)((8 * ((lane & 15) ^ (dma_row & 15))) * 2);
+    const unsigned pg_lane_v = (unsigned)((8 * ((lane & 15) ^ ((dma_row & 3) << 2))) * 2);
     auto issue = [&](__amdgpu_buffer_rsrc_t rs, int t, unsigned char* dst, bool is_v) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < SLOTS / NW; ++i) {
             const int sl = wave + NW * i;
-            unsigned rows = (unsigned)((t * BN + 4 * NW * i) * D * 2);
+            if constexpr (PAGED) {
+                const int j0 = t * BN + 4 * NW * i + 4 * wave;     // first row of the slot
+                const bool any = j0 < Sk;
+                const int page = any ? table[off_b + (j0 >> ps_log2)] : 0;
+                const uint16_t* tile = (is_v ? V : K) + ((size_t)page * Hkv + g) * ((size_t)ps * D);
+                const __amdgpu_buffer_rsrc_t pr =
+                    __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, any ? ps * D * 2 : 0, kRsrcWord3);
+                const int j = j0 + (lane >> 4);
+                const unsigned voff = j < Sk ? (unsigned)((j & (ps - 1)) * D * 2) + (is_v ? pg_lane_v : pg_lane_k)
+                                             : (unsigned)(ps * D * 2);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(pr, (lds_void*)(dst + sl * 1024), 16, voff, 0, 0, 0);
+            } else {
+                unsigned rows = (unsigned)((t * BN + 4 * NW * i) * D * 2);
 #if defined(__HIP_DEVICE_COMPILE__)
-            asm volatile("" : "+s"(rows));
+                asm volatile("" : "+s"(rows));
 #endif
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + sl * 1024), 16,
-                                                     (unsigned)((is_v ? kv_lane_v : kv_lane_k) + rows), 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + sl * 1024), 16,
+                                                         (unsigned)((is_v ? kv_lane_v : kv_lane_k) + rows), 0, 0, 0);
+            }
         }
     };
     // K operand (A: key = lane % 32) of S-step st, keys 32*kbk .. +31
@@ -749,7 +808,7 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         }
 }
 
-template <int NW, bool NEG>
+template <int NW, bool NEG, bool PAGED>
 hipError_t launch_pipe(const PrefillArgs& a, hipStream_t stream) {
     const int nqt = (a.Sq + 32 * NW - 1) / (32 * NW);
     const long long nitems = (long long)a.B * a.Hq * nqt;
@@ -758,9 +817,12 @@ hipError_t launch_pipe(const PrefillArgs& a, hipStream_t stream) {
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     float c2 = a.scale * 1.4426950408889634f;
     if (c2 == 0.f) c2 = 1e-30f;
-    hipLaunchKernelGGL((prefill_pipe_kernel<NW, NEG>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
+    int ps_log2 = 0;
+    while ((1 << ps_log2) < a.page_size) ++ps_log2;
+    hipLaunchKernelGGL((prefill_pipe_kernel<NW, NEG, PAGED>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                       a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)per_xcd);
+                       a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)per_xcd,
+                       a.page_table, a.seq_lens, ps_log2);
     return hipGetLastError();
 }
 
@@ -785,7 +847,18 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     const bool neg = a.scale < 0.f;
-    if (a.D == 128) return neg ? launch_pipe<8, true>(a, stream) : launch_pipe<8, false>(a, stream);
+    // D = 128: 256-row workgroups (eight waves) unless that leaves fewer than
+    // two workgroups per CU, then 128-row ones (four waves) for balance
+    const long long wg256 = (long long)a.B * a.Hq * ((a.Sq + 255) / 256);
+    const bool small = wg256 < 2LL * 256;
+    if (a.page_table != nullptr) {  // paged K/V (D = 128 only, checked by the caller)
+        if (small) return neg ? launch_pipe<4, true, true>(a, stream) : launch_pipe<4, false, true>(a, stream);
+        return neg ? launch_pipe<8, true, true>(a, stream) : launch_pipe<8, false, true>(a, stream);
+    }
+    if (a.D == 128) {
+        if (small) return neg ? launch_pipe<4, true, false>(a, stream) : launch_pipe<4, false, false>(a, stream);
+        return neg ? launch_pipe<8, true, false>(a, stream) : launch_pipe<8, false, false>(a, stream);
+    }
     return neg ? launch_t<64, true>(a, stream) : launch_t<64, false>(a, stream);
 }
 

@@ -26,6 +26,10 @@ WORKLOADS = {
                          len_lo=512, len_hi=8192, dtype="bf16", seed=126),
     "swa_16k_w4k": dict(kind="prefill", B=1, Hq=32, Hkv=8, Sq=16384, Sk=16384, D=128,
                         dtype="bf16", causal=True, window=4096, seed=127),
+    # chunked prefill: 512 new tokens per sequence against paged caches of
+    # 2048..6144 tokens (the new ones included)
+    "chunked_prefill_paged": dict(kind="paged_prefill", nseq=8, Sq=512, Hq=32, Hkv=8, D=128, page_size=16,
+                                  len_lo=2048, len_hi=6144, dtype="bf16", seed=128),
 }
 
 
@@ -85,8 +89,20 @@ def decode_inputs(nseq, Hq, Hkv, D, page_size, len_lo, len_hi, dtype="bf16", see
                 page_table=table.to(torch.int32), seq_lens=seq_lens.to(torch.int32))
 
 
+def paged_prefill_inputs(nseq, Sq, Hq, Hkv, D, page_size, len_lo, len_hi, dtype="bf16", seed=0):
+    """A paged cache as in decode_inputs (drawn first, same seed) plus q
+    [nseq, Hq, Sq, D] for the Sq newest tokens of each sequence."""
+    d = decode_inputs(nseq, Hq, Hkv, D, page_size, len_lo, len_hi, dtype, seed)
+    g = torch.Generator(device="cpu").manual_seed(seed + 1)
+    d["q"] = torch.randn((nseq, Hq, Sq, D), generator=g, dtype=torch.float32).to(_torch_dtype(dtype))
+    return d
+
+
 def workload_inputs(name):
     w = WORKLOADS[name]
+    if w["kind"] == "paged_prefill":
+        return paged_prefill_inputs(w["nseq"], w["Sq"], w["Hq"], w["Hkv"], w["D"], w["page_size"],
+                                    w["len_lo"], w["len_hi"], w["dtype"], w["seed"])
     if w["kind"] == "prefill":
         return prefill_inputs(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Sk"], w["D"],
                               w["dtype"], w["seed"])

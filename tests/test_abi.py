@@ -41,7 +41,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert _declared() == ["attn_decode_paged", "attn_decode_paged_window", "attn_fwd", "attn_fwd_f32",
-                           "attn_fwd_f32_lse", "attn_fwd_lse", "attn_kv_append", "attn_pages_create", "attn_pages_destroy", "attn_pages_free_count",
+                           "attn_fwd_f32_lse", "attn_fwd_lse", "attn_fwd_paged", "attn_kv_append", "attn_pages_create", "attn_pages_destroy", "attn_pages_free_count",
                            "attn_pages_resize", "attn_pages_table", "attn_release", "attn_strerror"]
     assert _codes() == {"ATTN_OK": OK, "ATTN_ERR_NULL": NULL, "ATTN_ERR_SHAPE": SHAPE, "ATTN_ERR_HEADS": HEADS,
                         "ATTN_ERR_HEADDIM": HEADDIM, "ATTN_ERR_MASK": MASK, "ATTN_ERR_SCALE": SCALE,
@@ -226,3 +226,26 @@ def test_fwd_lse_validation(lib, f32):
     # empty calls need no pointer at all
     assert _fwd_lse(lib, lse=None, f32=f32, q=None, k=None, v=None, o=None, B=0) == OK
     assert _fwd_lse(lib, lse=None, f32=f32, q=None, k=None, v=None, o=None, Sq=0) == OK
+
+
+def _fwdp(lib, q=A, kp=A, vp=A, pt=A, sl=A, o=A, lse=None, B=2, Hq=8, Hkv=2, Sq=16, D=128, ps=16, scale=0.1,
+          causal=1, window=0):
+    return lib.attn_fwd_paged(q, kp, vp, pt, sl, o, lse, B, Hq, Hkv, Sq, D, ps, scale, causal, window, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(q=None), NULL), (dict(kp=None), NULL), (dict(vp=None), NULL), (dict(pt=None), NULL),
+    (dict(sl=None), NULL), (dict(o=None), NULL),
+    (dict(B=-1), SHAPE), (dict(Sq=-1), SHAPE),
+    (dict(Hq=0), HEADS), (dict(Hq=8, Hkv=3), HEADS), (dict(D=64), HEADDIM), (dict(D=96), HEADDIM),
+    (dict(ps=4), PAGE), (dict(ps=48), PAGE), (dict(causal=2), MASK), (dict(causal=0, window=3), MASK),
+    (dict(window=-2), MASK), (dict(scale=float("nan")), SCALE),
+    (dict(q=U), ALIGN), (dict(kp=U), ALIGN), (dict(o=U), ALIGN), (dict(pt=A + 2), ALIGN), (dict(lse=A + 2), ALIGN),
+])
+def test_fwd_paged_validation(lib, kwargs, code):
+    assert _fwdp(lib, **kwargs) == code
+
+
+def test_fwd_paged_empty_calls(lib):
+    assert _fwdp(lib, q=None, kp=None, vp=None, pt=None, sl=None, o=None, B=0) == OK
+    assert _fwdp(lib, q=None, kp=None, vp=None, pt=None, sl=None, o=None, Sq=0) == OK

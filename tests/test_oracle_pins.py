@@ -499,3 +499,28 @@ def test_lse_closed_forms():
     k2 = np.array([[[[1.0], [0.99]]]])
     lse2 = oracle.attention_lse(q2, k2, k2, 1.0)
     np.testing.assert_allclose(lse2[0, 0, 0], 1000.0 + math.log1p(math.exp(-10.0)), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# prefill against a paged cache
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 5)])
+def test_paged_prefill_matches_brute_force_and_decode(causal, window):
+    rng = np.random.default_rng(18)
+    lens = [7, 16, 20]
+    B, Hq, Hkv, Sq, D, ps = len(lens), 4, 2, 3, 3, 8
+    Smax = max(lens)
+    kc = rng.standard_normal((B, Hkv, Smax, D))
+    vc = rng.standard_normal((B, Hkv, Smax, D))
+    q = rng.standard_normal((B, Hq, Sq, D))
+    kp, vp, table = _paged_from_contiguous(kc, vc, lens, ps, rng, True)
+    got = oracle.prefill_paged(q, kp, vp, table, np.array(lens), ps, 0.6, causal, window)
+    for b, n in enumerate(lens):
+        want = _brute(q[b:b + 1].tolist(), kc[b:b + 1, :, :n].tolist(), vc[b:b + 1, :, :n].tolist(), 0.6,
+                      causal, window)
+        np.testing.assert_allclose(got[b], want[0], atol=1e-12)
+    if causal:
+        # the last query row is the decode step of the last token
+        last = oracle.decode_paged_window(q[:, :, -1], kp, vp, table, np.array(lens), ps, 0.6, window)
+        np.testing.assert_allclose(got[:, :, -1], last, atol=1e-13)
