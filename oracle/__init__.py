@@ -14,6 +14,7 @@ from .attention import (  # noqa: F401
     softmax_rows,
     attention,
     attention_lse,
+    attention_bwd,
     attention_rows,
     attention_weights,
     sequence_pages,

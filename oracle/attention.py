@@ -271,3 +271,48 @@ def prefill_paged(q, k_pool, v_pool, page_table, seq_lens, page_size, scale, cau
         vb = gather_sequence(v_pool, page_table, seq_lens, page_size, b)[None]
         out[b] = attention(np.asarray(q[b:b + 1], dtype=np.float64), kb, vb, scale, causal, window)[0]
     return out
+
+
+def attention_bwd(q, k, v, do, scale, causal=False, window=0, row_chunk=2048):
+    """Gradients (dq, dk, dv), float64, of L = sum(do * O) where O is
+    `attention(q, k, v, scale, causal, window)`; shapes as q, k, v.
+
+    The pages name the backward pass only through FlashAttention's
+    recomputation ("Attention From Scratch", 进阶篇 §5; "LLM 核心技术", section
+    底层算子优化：FlashAttention) and the softmax gradient made of p(1 - p)
+    terms ("拆开 LLM（二）", section "√d 不是装饰，是保命符"). This is the plain
+    chain rule through the definition, per (batch, query head), with
+    S = scale * q k^T masked to -inf and P = softmax(S) by rows:
+
+    * dV = P^T dO and dP = dO V^T;
+    * dS = P * (dP - rowsum(P * dP)), the softmax Jacobian diag(p) - p p^T
+      applied row by row (masked entries have p = 0, hence dS = 0);
+    * dQ = scale * dS K and dK = scale * dS^T Q.
+
+    K/V head g is read by the query heads h with h // (Hq // Hkv) == g
+    (repeat_interleave on the head axis, "Attention 机制详解" §5.2), so its dK
+    and dV are the sums over those heads. ``row_chunk`` only bounds memory:
+    rows contribute to dK and dV independently.
+    """
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    dq = np.zeros((B, Hq, Sq, D), dtype=np.float64)
+    dk = np.zeros((B, Hkv, Sk, D), dtype=np.float64)
+    dv = np.zeros((B, Hkv, Sk, v.shape[3]), dtype=np.float64)
+    vis = visible(Sq, Sk, causal, window)
+    for b in range(B):
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            kb = np.asarray(k[b, g], dtype=np.float64)
+            vb = np.asarray(v[b, g], dtype=np.float64)
+            for r0 in range(0, Sq, row_chunk):
+                r1 = min(Sq, r0 + row_chunk)
+                qr = np.asarray(q[b, h, r0:r1], dtype=np.float64)
+                dor = np.asarray(do[b, h, r0:r1], dtype=np.float64)
+                p = softmax_rows(_scores(qr, kb, scale, vis[r0:r1]))
+                dv[b, g] += p.T @ dor
+                dp = dor @ vb.T
+                ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+                dq[b, h, r0:r1] = scale * (ds @ kb)
+                dk[b, g] += scale * (ds.T @ qr)
+    return dq, dk, dv

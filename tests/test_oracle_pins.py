@@ -524,3 +524,151 @@ def test_paged_prefill_matches_brute_force_and_decode(causal, window):
         # the last query row is the decode step of the last token
         last = oracle.decode_paged_window(q[:, :, -1], kp, vp, table, np.array(lens), ps, 0.6, window)
         np.testing.assert_allclose(got[:, :, -1], last, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# backward pass: gradients of L = sum(dO * O)
+
+
+def _loss_brute(q, k, v, do, scale, causal, window):
+    return float(np.sum(do * _brute(q.tolist(), k.tolist(), v.tolist(), scale, causal, window)))
+
+
+def _fd_grads(q, k, v, do, scale, causal, window, h=1e-5):
+    """Central differences of the brute-force forward, element by element."""
+    grads = []
+    for x in (q, k, v):
+        g = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            keep = x[idx]
+            x[idx] = keep + h
+            up = _loss_brute(q, k, v, do, scale, causal, window)
+            x[idx] = keep - h
+            dn = _loss_brute(q, k, v, do, scale, causal, window)
+            x[idx] = keep
+            g[idx] = (up - dn) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+def _bwd_inputs(case, seed_extra=0):
+    B, Hq, Hkv, Sq, Sk, D, causal, window = case
+    rng = np.random.default_rng(sum(case[:6]) + 100 + seed_extra)
+    q = rng.standard_normal((B, Hq, Sq, D))
+    k = rng.standard_normal((B, Hkv, Sk, D))
+    v = rng.standard_normal((B, Hkv, Sk, D))
+    do = rng.standard_normal((B, Hq, Sq, D))
+    return q, k, v, do
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_bwd_matches_finite_differences_of_brute_force(case):
+    causal, window = case[6], case[7]
+    q, k, v, do = _bwd_inputs(case)
+    scale = 0.7
+    want = _fd_grads(q, k, v, do, scale, causal, window)
+    got = oracle.attention_bwd(q, k, v, do, scale, causal, window)
+    for g, w in zip(got, want):
+        np.testing.assert_allclose(g, w, rtol=0, atol=2e-7)
+
+
+def test_bwd_pins_reject_plausible_slips():
+    # the finite-difference pin fails for each of these variants of the chain
+    # rule, computed here beside the oracle's arithmetic
+    case = (1, 2, 1, 5, 6, 3, True, 0)
+    q, k, v, do = _bwd_inputs(case)
+    scale = 0.7
+    fd = _fd_grads(q, k, v, do, scale, True, 0)
+    vis = oracle.visible(5, 6, True, 0)
+
+    def grads(variant):
+        dq = np.zeros_like(q)
+        dk = np.zeros_like(k)
+        dv = np.zeros_like(v)
+        for hq in range(2):
+            p = oracle.attention_weights(q[0, hq], k[0, 0], scale, True)
+            dp = do[0, hq] @ v[0, 0].T
+            rs = np.sum(p * dp, axis=1, keepdims=True)
+            ds = p * dp if variant == "no_rowsum" else p * (dp - rs)
+            if variant == "mask_after":  # Jacobian applied as if masked keys had weight
+                ds = np.where(vis, ds, dp)
+            s = 1.0 if variant == "no_scale" else scale
+            dk[0, 0] += s * ds.T @ q[0, hq]
+            dq[0, hq] = s * ds @ (v[0, 0] if variant == "dq_from_v" else k[0, 0])
+            dv[0, 0] += (dp if variant == "dv_from_dp" else p).T @ do[0, hq]
+        return dq, dk, dv
+
+    def close(gs):
+        return all(np.allclose(g, w, rtol=0, atol=2e-7) for g, w in zip(gs, fd))
+
+    assert close(oracle.attention_bwd(q, k, v, do, scale, True, 0))
+    assert close(grads("none"))
+    for variant in ("no_rowsum", "mask_after", "no_scale", "dv_from_dp", "dq_from_v"):
+        assert not close(grads(variant)), variant
+
+
+def test_bwd_two_keys_closed_form():
+    # one query, two keys: O = s v0 + (1 - s) v1 with s = sigma(z),
+    # z = scale q . (k0 - k1); dO . dO/dz = s (1 - s) dO . (v0 - v1), the
+    # p (1 - p) factor of the softmax gradient
+    q = np.array([[[[0.3, -1.2, 0.5]]]])
+    k = np.array([[[[1.0, 0.4, -0.7], [-0.2, 0.9, 0.1]]]])
+    v = np.array([[[[2.0, -1.0, 0.5], [0.25, 3.0, -2.0]]]])
+    do = np.array([[[[0.7, -0.4, 1.1]]]])
+    scale = 0.9
+    z = scale * float(q[0, 0, 0] @ (k[0, 0, 0] - k[0, 0, 1]))
+    s = 1.0 / (1.0 + math.exp(-z))
+    t = s * (1.0 - s) * float(do[0, 0, 0] @ (v[0, 0, 0] - v[0, 0, 1]))
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, scale)
+    np.testing.assert_allclose(dq[0, 0, 0], scale * t * (k[0, 0, 0] - k[0, 0, 1]), atol=1e-14)
+    np.testing.assert_allclose(dk[0, 0, 0], scale * t * q[0, 0, 0], atol=1e-14)
+    np.testing.assert_allclose(dk[0, 0, 1], -scale * t * q[0, 0, 0], atol=1e-14)
+    np.testing.assert_allclose(dv[0, 0, 0], s * do[0, 0, 0], atol=1e-14)
+    np.testing.assert_allclose(dv[0, 0, 1], (1.0 - s) * do[0, 0, 0], atol=1e-14)
+
+
+def test_bwd_special_cases():
+    rng = np.random.default_rng(41)
+    B, Hq, Hkv, S, D = 2, 4, 2, 6, 3
+    q = rng.standard_normal((B, Hq, S, D))
+    k = rng.standard_normal((B, Hkv, S, D))
+    v = rng.standard_normal((B, Hkv, S, D))
+    do = rng.standard_normal((B, Hq, S, D))
+    group_sum = do.reshape(B, Hkv, Hq // Hkv, S, D).sum(axis=2)
+    # a single key: O = V[0] for every row, nothing depends on q or k
+    dq, dk, dv = oracle.attention_bwd(q, k[:, :, :1], v[:, :, :1], do, 0.8)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    np.testing.assert_allclose(dv[:, :, 0], group_sum.sum(axis=2), atol=1e-13)
+    # window 1: O = V, the same
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, 0.8, causal=True, window=1)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    np.testing.assert_allclose(dv, group_sum, atol=1e-13)
+    # scale 0: uniform weights over the visible keys, no gradient to q or k
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, 0.0, causal=True)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    want = np.zeros_like(v)
+    for i in range(S):
+        want[:, :, : i + 1] += group_sum[:, :, i : i + 1] / (i + 1)
+    np.testing.assert_allclose(dv, want, atol=1e-13)
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_bwd_invariants(case):
+    B, Hq, Hkv, Sq, Sk, D, causal, window = case
+    q, k, v, do = _bwd_inputs(case, seed_extra=7)
+    scale = 0.45
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, scale, causal, window)
+    o = oracle.attention(q, k, v, scale, causal, window)
+    G = Hq // Hkv
+    # adding one vector to every key shifts each row's logits by a constant,
+    # which the softmax ignores: the key gradients of a head sum to zero
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+    # logits depend on q and k only through scale * q k^T: scaling q and
+    # scaling k act alike, so sum(dq * q) = sum(dk * k) per K/V head
+    lhs = (dq * q).reshape(B, Hkv, G, Sq, D).sum(axis=(2, 3, 4))
+    rhs = (dk * k).sum(axis=(2, 3))
+    np.testing.assert_allclose(lhs, rhs, atol=1e-12)
+    # O is linear in V: sum(dv * v) = L = sum(do * O)
+    np.testing.assert_allclose((dv * v).sum(), (do * o).sum(), atol=1e-12)
