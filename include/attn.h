@@ -252,6 +252,37 @@ int attn_pages_free_count(const attn_page_pool* pool);
 int attn_pages_table(const attn_page_pool* pool, const int64_t* seq_ids, int n, int32_t* page_table,
                      int64_t table_cap, int32_t* seq_lens, int64_t* table_len);
 
+/*
+ * attn_bwd — backward pass of attn_fwd: the gradients dq, dk, dv of
+ * L = sum(dout * o) for o = attn_fwd(q, k, v, ...). The pages name the
+ * backward only through FlashAttention's recomputation ("Attention From
+ * Scratch", 进阶篇 §5; "LLM 核心技术", section 底层算子优化：FlashAttention):
+ * the weights P are recomputed from q, k and the forward's lse instead of
+ * being stored. With S = scale * q k^T (masked as in attn_fwd) and
+ * P = exp(S - lse): dv = P^T dout, dS = P * (dout v^T - rowsum(dout * o)),
+ * dq = scale * dS k, dk = scale * dS^T q; dk and dv of a K/V head sum over
+ * the query heads that read it (GQA).
+ *   q, o, dout, dq : [B, Hq, Sq, D] bfloat16, device, 16-byte aligned.
+ *   k, v, dk, dv   : [B, Hkv, Sk, D] bfloat16, device, 16-byte aligned.
+ *   lse            : [B, Hq, Sq] float32, device, 4-byte aligned: the lse that
+ *                    attn_fwd_lse returned with this o (natural logarithm).
+ *   dq, dk, dv are written in full (keys no query sees get zero gradients);
+ *   they must not overlap the inputs. Arithmetic: bf16 MFMA products with
+ *   float32 accumulation; P and dS are rounded to bf16 as MFMA operands, and
+ *   rowsum(dout * o) uses the bf16 o.
+ *   Scratch: B * Hq * Sq floats of the per-(device, stream) workspace that
+ *   attn_decode_paged also uses (grown on demand, freed by attn_release).
+ *   Errors: those of attn_fwd for the same sizes, plus NULL / ALIGN for the
+ *   extra pointers, NOMEM for the workspace, and SHAPE when Sq * D or Sk * D
+ *   exceeds 2^29 (one head's rows are addressed with 32-bit offsets).
+ *   B == 0 is a no-op; Sq == 0 writes zero dk and dv and then accepts NULL
+ *   for q, k, v, o, dout, lse and dq.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv,
+             int B, int Hq, int Hkv, int Sq, int Sk, int D,
+             float scale, int causal, int window, hipStream_t stream);
+
 /* attn_strerror — static, never-NULL description of a status code. */
 const char* attn_strerror(int status);
 

@@ -14,7 +14,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fwd_f32", "decode_paged", "strerror", "release", "library_path", "load_library"]
+__all__ = ["fwd", "fwd_f32", "bwd", "decode_paged", "strerror", "release", "library_path", "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -55,6 +55,8 @@ def load_library():
     lib.attn_fwd_paged.restype = i32
     lib.attn_kv_append.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
     lib.attn_kv_append.restype = i32
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
+    lib.attn_bwd.restype = i32
     i64, pp = ctypes.c_int64, ctypes.POINTER(ctypes.c_void_p)
     lib.attn_pages_create.argtypes = [i32, i32, pp]
     lib.attn_pages_create.restype = i32
@@ -166,6 +168,47 @@ def fwd_f32(q, k, v, o=None, scale=None, causal=False, window=0):
     import torch
 
     return _prefill(load_library().attn_fwd_f32, torch.float32, q, k, v, o, scale, causal, window)
+
+
+def bwd(q, k, v, o, do, lse, scale=None, causal=False, window=0, dq=None, dk=None, dv=None):
+    """Backward pass of fwd: (dq, dk, dv) for upstream gradient do.
+
+    q, o, do [B,Hq,Sq,D] and k, v [B,Hkv,Sk,D] bfloat16; lse [B,Hq,Sq] float32
+    as returned by fwd_lse with this o. dq, dk, dv are allocated when None.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _need(t, name, torch.bfloat16)
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, S, D]")
+    _need(lse, "lse", torch.float32)
+    B, Hq, Sq, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    if o.shape != q.shape or do.shape != q.shape:
+        raise ValueError("o and do must have the shape of q")
+    if tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("lse must be [B, Hq, Sq]")
+    Hkv, Sk = k.shape[1], k.shape[2]
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _need(t, name, torch.bfloat16)
+        if t.shape != like.shape:
+            raise ValueError(f"{name} must have the shape of {'q' if like is q else 'k'}")
+    if len({t.device for t in (q, k, v, o, do, lse, dq, dk, dv)}) != 1:
+        raise ValueError("all tensors must be on one device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        rc = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Sq, Sk, D, float(scale),
+                          int(bool(causal)), int(window), _stream(q))
+    _check(rc, "attn_bwd")
+    return dq, dk, dv
 
 
 def _decode_args(q, k_pool, v_pool, page_table, seq_lens, scale, o):

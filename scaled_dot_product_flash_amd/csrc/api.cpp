@@ -212,6 +212,42 @@ int attn_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_p
     return hip_status(attn::launch_kv_append(a, stream));
 }
 
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale, int causal,
+             int window, hipStream_t stream) {
+    if (B < 0 || Sq < 0 || Sk < 0) return ATTN_ERR_SHAPE;
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_HEADS;
+    if (D != 64 && D != 128) return ATTN_ERR_HEADDIM;
+    if (causal != 0 && causal != 1) return ATTN_ERR_MASK;
+    if (window < 0 || (window > 0 && !causal)) return ATTN_ERR_MASK;
+    if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+    if (B == 0 || (Sq == 0 && Sk == 0)) return ATTN_OK;
+    if (Sk < 1) return ATTN_ERR_SHAPE;
+    if (causal && Sq > Sk) return ATTN_ERR_SHAPE;
+    if (!product_fits(B, Hq, Sq, D) || !product_fits(B, Hkv, Sk, D)) return ATTN_ERR_SHAPE;
+    // one head's Q/dO or K/V rows (plus a tile of overrun) are addressed with
+    // 32-bit byte offsets
+    if ((long long)Sk * D * 4 > 0x7FFFFFFFLL || (long long)Sq * D * 4 > 0x7FFFFFFFLL) return ATTN_ERR_SHAPE;
+    const long long items = (long long)B * Hq * ((Sq + 127) / 128) + (long long)B * Hkv * ((Sk + 127) / 128) + 16;
+    if (items > 0x7FFFFFFFLL) return ATTN_ERR_SHAPE;
+    // with no query rows only dk and dv (zeros) are written; the query-side
+    // tensors are empty and their pointers may be NULL
+    const bool rows = Sq > 0;
+    if (!dk || !dv || (rows && (!q || !k || !v || !o || !dout || !lse || !dq))) return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned4(lse) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return ATTN_ERR_ALIGN;
+    float* delta = nullptr;
+    if (Sq > 0) {
+        int device = 0;
+        if (hipGetDevice(&device) != hipSuccess) return ATTN_ERR_HIP;
+        const int rc = get_workspace(device, stream, (size_t)B * Hq * Sq, &delta);
+        if (rc != ATTN_OK) return rc;
+    }
+    attn::BackwardArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, delta};
+    return hip_status(attn::launch_backward(a, stream));
+}
+
 const char* attn_strerror(int status) {
     switch (status) {
         case ATTN_OK: return "success";
@@ -223,7 +259,7 @@ const char* attn_strerror(int status) {
         case ATTN_ERR_SCALE: return "scale is not finite";
         case ATTN_ERR_PAGE: return "page_size must be a power of two in [8, 256]";
         case ATTN_ERR_ALIGN: return "a tensor pointer is not sufficiently aligned (16 bytes; 4 for int32 tables)";
-        case ATTN_ERR_NOMEM: return "device memory for the decode workspace could not be allocated";
+        case ATTN_ERR_NOMEM: return "device memory for the library workspace could not be allocated";
         case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
         case ATTN_ERR_FULL: return "the page pool has too few free pages";
         case ATTN_ERR_SEQ: return "the page pool holds no sequence with this id";

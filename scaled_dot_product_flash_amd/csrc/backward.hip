@@ -1,0 +1,567 @@
+// Attention backward pass, bfloat16 in/out, on gfx950 MFMA.
+//
+// What it computes: for O = softmax(mask(Q K^T * scale)) V per (batch, query
+// head) and an upstream gradient dO, the gradients dQ, dK, dV of
+// L = sum(dO * O). With P the softmax weights and S the scaled logits:
+// dV = P^T dO, dP = dO V^T, dS = P * (dP - Delta) with
+// Delta_i = sum_j P_ij dP_ij = dO_i . O_i, dQ = scale * dS K and
+// dK = scale * dS^T Q; a K/V head collects the sums over the query heads that
+// read it (GQA, "Attention 机制详解：从 Self-Attention 到 Multi-Query
+// Attention" §5.2). P is not stored by the forward pass: it is recomputed
+// tile by tile from Q, K and the forward's per-row log-sum-exp, the
+// recomputation that the FlashAttention sections of "Attention From Scratch"
+// (进阶篇 §5) and "LLM 核心技术：Attention 机制的实现与优化" name as the
+// backward half of the method; P = exp2(S * c2 - lse * log2(e)) with
+// c2 = scale * log2(e).
+//
+// Two kernels run in order on the caller's stream:
+//  * bwd_dq_kernel, one workgroup per (batch, query head, 128 query rows),
+//    four waves of 32 rows. It forms Delta for its rows from dO and O (and
+//    stores it for the second kernel), keeps its Q and dO rows in registers,
+//    and streams 64-key tiles of K and V through LDS as the forward pass
+//    does: S^T = K Q^T and dP^T = V dO^T on MFMA (a lane owns one query),
+//    then dS, then dQ^T += K^T dS^T with the K^T operand read by the
+//    transposing LDS read.
+//  * bwd_dkdv_kernel, one workgroup per (batch, kv head, 128 keys), four
+//    waves of 32 keys. Its K and V rows stay in registers; it streams 64-row
+//    tiles of Q, dO, lse and Delta of every query head of the group through
+//    LDS: S = Q K^T and dP = dO V^T (a lane owns one key), P, dS, then
+//    dV^T += dO^T P and dK^T += Q^T dS with the transposed operands read by
+//    the transposing LDS read. Summing the group's heads inside one
+//    workgroup makes dK and dV plain stores, with no atomics.
+//
+// Both kernels take the 32x32x16 bf16 MFMA. Tiles are staged by buffer->LDS
+// DMA (rows past the end of a slice read as zeros through the buffer range
+// check), double buffered. 16-byte chunks of a tile row are XOR-swizzled so
+// that both reads of a tile, 32 rows at one chunk (row operand) and 4 rows x
+// 16 columns per 16 lanes (transposing read), avoid bank conflicts. Waves
+// skip 32x32 blocks with no visible pair; only blocks that straddle a mask
+// boundary or a tail evaluate the mask.
+
+#include "launch.h"
+
+#include <cmath>
+
+namespace attn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kNW = 4;                 // waves per workgroup
+constexpr int kThreads = 64 * kNW;
+constexpr int kRows = 32 * kNW;        // query rows (dq) or keys (dkdv) per workgroup
+constexpr int kTile = 64;              // rows of a streamed K/V or Q/dO tile
+constexpr int kXcds = 8;
+constexpr float kLog2e = 1.4426950408889634f;
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format).
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+__device__ __forceinline__ uint4 ld_global16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
+}
+
+// XOR swizzle of the 16-byte chunks of tile row `row` (row index within a
+// tile that starts at a multiple of 16 rows).
+//  * Row operand: 16 lanes read rows r .. r+15 at one logical chunk; the
+//    swizzle is a bijection on the low row bits, so they hit 16 different
+//    16-byte bank groups (D = 128: one row spans all banks; D = 64: two rows
+//    do, and the row parity supplies the missing bit).
+//  * Transposing read: 16 lanes read rows r0 .. r0+3 (r0 a multiple of 4),
+//    two adjacent chunks each; the swizzle sends the four rows' chunk pairs
+//    to four different pairs (D = 128: bits 1-2 carry row & 3; D = 64: rows
+//    r0, r0+2 share a parity and differ in bit 1).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (D == 128) return ((row & 3) << 1) | ((row >> 2) & 1) | (row & 8);
+    else return (((row >> 1) & 1) << 1) | ((row >> 2) & 1) | (((row >> 3) & 1) << 2);
+}
+
+// MFMA row operand: 8 bf16 of tile row `row`, logical chunk `chunk`.
+template <int D>
+__device__ __forceinline__ bf16x8 row_op(const unsigned char* t, int row, int chunk) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(t + row * (D * 2) + ((chunk ^ swz<D>(row)) << 4)));
+}
+
+// MFMA operand of the transposed tile for one 16-row k step starting at tile
+// row `row16`, 32-column block `db`: lane (l % 32, half hh) gets column
+// 32*db + l % 32 at rows row16 + 4hh + {0..3} and row16 + 8 + 4hh + {0..3},
+// the order in which a 32x32 accumulator hands a lane its rows.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_op(const unsigned char* t, int row16, int db, int lane) {
+    const int hh = lane >> 5, grp = (lane >> 4) & 1, e4 = (lane & 15) >> 2, q4 = lane & 3;
+    const int r = row16 + 4 * hh + e4;
+    const int d = 32 * db + 16 * grp + 4 * q4;
+    const int o_lo = r * (D * 2) + (((d >> 3) ^ swz<D>(r)) << 4) + ((d & 7) << 1);
+    const int o_hi = (r + 8) * (D * 2) + (((d >> 3) ^ swz<D>(r + 8)) << 4) + ((d & 7) << 1);
+    const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + o_lo));
+    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + o_hi));
+    const s16x8 a8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    return __builtin_bit_cast(bf16x8, a8);
+}
+
+// Stage rows r_first .. r_first + kTile - 1 of a [rows, D] bf16 slice into
+// `dst`, 1 KiB per wave instruction; the LDS side of a DMA is always
+// base + 16 * lane, so the swizzle is applied through the source offset.
+template <int D>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, int r_first, unsigned char* dst, int wave,
+                                         int lane) {
+    constexpr int CPR = D / 8;                   // 16-byte chunks per row
+    constexpr int RPS = 64 / CPR;                // rows per 1 KiB slot
+    constexpr int SLOTS = kTile * D * 2 / 1024;
+    static_assert(SLOTS % kNW == 0, "DMA slots per wave");
+#pragma unroll
+    for (int i = 0; i < SLOTS / kNW; ++i) {
+        const int sl = wave + kNW * i;
+        const int row = sl * RPS + lane / CPR;
+        const int chunk = (lane % CPR) ^ swz<D>(row);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + sl * 1024), 16,
+                                                 (unsigned)(((r_first + row) * D + 8 * chunk) * 2), 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+    const f32x2 x = {a, b}, y = {c, d};
+    uint2 r;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(y, bf16x2));
+    return r;
+}
+
+// 8 values of a 32x32 accumulator (k step `c` of its rows) as a bf16 operand
+__device__ __forceinline__ bf16x8 pack8(const f32x16& x, int c) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const f32x2 p = {x[8 * c + e], x[8 * c + e + 1]};
+        const bf16x2 b = __builtin_convertvector(p, bf16x2);
+        r[e] = b[0];
+        r[e + 1] = b[1];
+    }
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and Delta)
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2)
+void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                   const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
+                   float* __restrict__ Delta, uint16_t* __restrict__ dQ, int Hq, int Hkv, int Sq, int Sk,
+                   float scale, float c2, int causal, int window, int nqt, int nitems, int per_xcd) {
+    constexpr int BN = kTile, KB = BN / 32, DS = D / 16, DB = D / 32;
+    constexpr int TILE_BYTES = BN * D * 2;
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds1[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds1[TILE_BYTES];
+
+    // work item: (batch, kv head) major, then query tile from the heaviest
+    // causal one down, then the query heads of the group; each XCD takes a
+    // contiguous run of items
+    const int w = blockIdx.x;
+    const int item = (w % kXcds) * per_xcd + w / kXcds;
+    if (item >= nitems) return;
+    const int G = Hq / Hkv;
+    const int hg = item % G;
+    const int r1 = item / G;
+    const int qt = nqt - 1 - (r1 % nqt);
+    const int bg = r1 / nqt;
+    const int g = bg % Hkv;
+    const int b = bg / Hkv;
+    const int h = g * G + hg;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int ln = lane & 31;
+    const int hh = lane >> 5;
+
+    const int off = Sk - Sq;  // bottom-right causal alignment
+    const int i0 = qt * kRows;
+    const int row_end = min(i0 + kRows, Sq);
+    const size_t qo_base = ((size_t)b * Hq + h) * (size_t)Sq * D;
+    const size_t kv_base = ((size_t)b * Hkv + g) * (size_t)Sk * D;
+    const __amdgpu_buffer_rsrc_t krs = rsrc(K + kv_base, Sk * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = rsrc(V + kv_base, Sk * D * 2);
+
+    const int p_first = i0 + off, p_last = row_end - 1 + off;
+    const int hi = causal ? min(Sk, p_last + 1) : Sk;
+    const int lo = (causal && window > 0) ? max(0, p_first - window + 1) : 0;
+    const int t_begin = lo / BN;
+    const int t_end = (hi + BN - 1) / BN;
+
+    const int wr0 = i0 + 32 * wave;
+    const int wr1 = min(wr0 + 32, Sq) - 1;
+    const bool wave_rows = wr0 < Sq;
+    const int wp0 = wr0 + off, wp1 = wr1 + off;
+    const int w_hi = causal ? min(Sk - 1, wp1) : Sk - 1;
+    const int w_lo = (causal && window > 0) ? max(0, wp0 - window + 1) : 0;
+    const int w_full_hi = causal ? min(Sk - 1, wp0) : Sk - 1;
+    const int w_full_lo = (causal && window > 0) ? max(0, wp1 - window + 1) : 0;
+
+    // this lane's query row: Q and dO as MFMA B operands (8 d per lane per
+    // 16-wide step), Delta = dO . O, lse in log2 units
+    const int qrow = wr0 + ln;
+    const int qpos = qrow + off;
+    const bool row_ok = qrow < Sq;
+    bf16x8 qreg[DS], doreg[DS];
+    float dsum = 0.f;
+    {
+        const size_t rb = qo_base + (size_t)(row_ok ? qrow : 0) * D + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+            const uint4 z = make_uint4(0, 0, 0, 0);
+            qreg[s] = as_bf16x8(row_ok ? ld_global16(Q + rb + 16 * s) : z);
+            doreg[s] = as_bf16x8(row_ok ? ld_global16(dO + rb + 16 * s) : z);
+            const bf16x8 ob = as_bf16x8(row_ok ? ld_global16(O + rb + 16 * s) : z);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dsum = fmaf((float)doreg[s][e], (float)ob[e], dsum);
+        }
+    }
+    const float delta = dsum + __shfl_xor(dsum, 32);
+    const size_t row_idx = ((size_t)b * Hq + h) * Sq + qrow;
+    if (row_ok && hh == 0) Delta[row_idx] = delta;
+    const float lse2 = row_ok ? LSE[row_idx] * kLog2e : 0.f;
+
+    f32x16 dq[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dq[db][v] = 0.f;
+
+    auto issue = [&](int t, unsigned char* kd, unsigned char* vd) __attribute__((always_inline)) {
+        dma_tile<D>(krs, t * BN, kd, wave, lane);
+        dma_tile<D>(vrs, t * BN, vd, wave, lane);
+    };
+
+    // one 32-key block of a tile (keys j0 + 32x .. +31 at tile rows 32x ..)
+    auto block = [&](const unsigned char* kb, const unsigned char* vb, int j0, int x, bool edge)
+        __attribute__((always_inline)) {
+        f32x16 s, dp;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            s[v] = 0.f;
+            dp[v] = 0.f;
+        }
+#pragma unroll
+        for (int st = 0; st < DS; ++st) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op<D>(kb, 32 * x + ln, 2 * st + hh), qreg[st], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op<D>(vb, 32 * x + ln, 2 * st + hh), doreg[st], dp, 0,
+                                                         0, 0);
+        }
+        // exponent of P; masked pairs get -inf, so P = 0 and dS = 0 exactly
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] = fmaf(s[v], c2, -lse2);
+        if (edge) {
+            asm volatile("");
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int j = j0 + 32 * x + 8 * (v >> 2) + 4 * hh + (v & 3);
+                bool ok = j < Sk;
+                if (causal) ok = ok && j <= qpos;
+                if (window > 0) ok = ok && j > qpos - window;
+                s[v] = ok ? s[v] : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] = __builtin_amdgcn_exp2f(s[v]) * (dp[v] - delta);
+        // dQ^T += K^T dS^T; k step c covers keys 32x + 16c .. +15 of the tile
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const bf16x8 dsb = pack8(s, c);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_op<D>(kb, 32 * x + 16 * c, db, lane), dsb, dq[db],
+                                                                 0, 0, 0);
+        }
+    };
+
+    auto step = [&](int t, unsigned char* kc, unsigned char* vc, unsigned char* kn, unsigned char* vn)
+        __attribute__((always_inline)) {
+        if (t + 1 < t_end) issue(t + 1, kn, vn);
+        const int j0 = t * BN;
+        const bool active = wave_rows && j0 <= w_hi && j0 + BN - 1 >= w_lo;
+        if (active) {
+#pragma unroll
+            for (int x = 0; x < KB; ++x) {
+                const int jb = j0 + 32 * x;
+                if (jb > w_hi || jb + 31 < w_lo) continue;
+                const bool edge = (jb + 31 > w_full_hi) || (jb < w_full_lo);
+                block(kc, vc, j0, x, edge);
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+
+    if (t_begin < t_end) {
+        issue(t_begin, k_lds0, v_lds0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        for (int t = t_begin; t < t_end; t += 2) {
+            step(t, k_lds0, v_lds0, k_lds1, v_lds1);
+            if (t + 1 < t_end) step(t + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+        }
+    }
+
+    if (!row_ok) return;
+    uint16_t* out = dQ + qo_base + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            *reinterpret_cast<uint2*>(out + 32 * db + 8 * r + 4 * hh) =
+                pack4(dq[db][4 * r] * scale, dq[db][4 * r + 1] * scale, dq[db][4 * r + 2] * scale,
+                      dq[db][4 * r + 3] * scale);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV
+
+template <int D>
+__global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2)
+void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                     const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dK,
+                     uint16_t* __restrict__ dV, int Hq, int Hkv, int Sq, int Sk, float scale, float c2, int causal,
+                     int window, int nkt, int nitems, int per_xcd) {
+    constexpr int BM = kTile, DS = D / 16, DB = D / 32;
+    constexpr int TILE_BYTES = BM * D * 2;
+    __shared__ __attribute__((aligned(16))) unsigned char q_lds0[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char q_lds1[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char o_lds0[TILE_BYTES];  // dO
+    __shared__ __attribute__((aligned(16))) unsigned char o_lds1[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) float l_lds0[BM];                    // lse
+    __shared__ __attribute__((aligned(16))) float l_lds1[BM];
+    __shared__ __attribute__((aligned(16))) float d_lds0[BM];                    // Delta
+    __shared__ __attribute__((aligned(16))) float d_lds1[BM];
+
+    // work item: (batch, kv head) major, key block ascending (under a causal
+    // mask the first keys are seen by the most queries); each XCD takes a
+    // contiguous run, so the key blocks of one head share Q and dO in its L2
+    const int w = blockIdx.x;
+    const int item = (w % kXcds) * per_xcd + w / kXcds;
+    if (item >= nitems) return;
+    const int G = Hq / Hkv;
+    const int kt = item % nkt;
+    const int bg = item / nkt;
+    const int g = bg % Hkv;
+    const int b = bg / Hkv;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int ln = lane & 31;
+    const int hh = lane >> 5;
+
+    const int off = Sk - Sq;
+    const int k0 = kt * kRows;
+    const int kw0 = k0 + 32 * wave;                 // first key of this wave
+    const int kw1 = min(kw0 + 31, Sk - 1);
+    const bool wave_keys = kw0 < Sk;
+    const int key = kw0 + ln;
+    const bool key_ok = key < Sk;
+
+    // this lane's key row: K and V as MFMA B operands
+    const size_t kv_base = ((size_t)b * Hkv + g) * (size_t)Sk * D;
+    bf16x8 kreg[DS], vreg[DS];
+    {
+        const size_t rb = kv_base + (size_t)(key_ok ? key : 0) * D + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+            const uint4 z = make_uint4(0, 0, 0, 0);
+            kreg[s] = as_bf16x8(key_ok ? ld_global16(K + rb + 16 * s) : z);
+            vreg[s] = as_bf16x8(key_ok ? ld_global16(V + rb + 16 * s) : z);
+        }
+    }
+
+    // queries that see at least one key of the workgroup: position p = q + off
+    // sees key j iff j <= p (causal) and j > p - window
+    const int kmax = min(k0 + kRows, Sk) - 1;
+    const int q_lo = causal ? max(0, k0 - off) : 0;
+    const int q_hi = (causal && window > 0) ? min(Sq - 1, kmax + window - 1 - off) : Sq - 1;
+    const int tq0 = q_lo / BM;
+    const int nt = q_lo <= q_hi ? q_hi / BM - tq0 + 1 : 0;
+    const int nsteps = G * nt;
+
+    f32x16 dk[DB], dv[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            dk[db][v] = 0.f;
+            dv[db][v] = 0.f;
+        }
+
+    auto issue = [&](int s, unsigned char* qd, unsigned char* od, float* ld, float* dd) __attribute__((always_inline)) {
+        const int hidx = s / nt;
+        const int t = tq0 + s - hidx * nt;
+        const size_t rows = ((size_t)b * Hq + g * G + hidx) * (size_t)Sq;
+        dma_tile<D>(rsrc(Q + rows * D, Sq * D * 2), t * BM, qd, wave, lane);
+        dma_tile<D>(rsrc(dO + rows * D, Sq * D * 2), t * BM, od, wave, lane);
+        if (wave == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(LSE + rows, Sq * 4), (lds_void*)ld, 4,
+                                                     (unsigned)((t * BM + lane) * 4), 0, 0, 0);
+        else if (wave == 1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(Delta + rows, Sq * 4), (lds_void*)dd, 4,
+                                                     (unsigned)((t * BM + lane) * 4), 0, 0, 0);
+    };
+
+    // one 32-query block at tile rows r0 .. r0+31 (queries qa .. qa+31)
+    auto block = [&](const unsigned char* qb, const unsigned char* ob, const float* lb, const float* db_,
+                     int r0, int qa, bool edge) __attribute__((always_inline)) {
+        f32x16 s, dp;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            s[v] = 0.f;
+            dp[v] = 0.f;
+        }
+#pragma unroll
+        for (int st = 0; st < DS; ++st) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op<D>(qb, r0 + ln, 2 * st + hh), kreg[st], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op<D>(ob, r0 + ln, 2 * st + hh), vreg[st], dp, 0, 0, 0);
+        }
+        // accumulator value v holds query row r0 + 8(v/4) + 4hh + v%4
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 l4 = *reinterpret_cast<const float4*>(lb + r0 + 8 * j + 4 * hh);
+            const float l[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[4 * j + i] = fmaf(s[4 * j + i], c2, -l[i] * kLog2e);
+        }
+        if (edge) {
+            asm volatile("");
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int q = qa + 8 * (v >> 2) + 4 * hh + (v & 3);
+                const int p = q + off;
+                bool ok = q < Sq && key_ok;
+                if (causal) ok = ok && key <= p;
+                if (window > 0) ok = ok && key > p - window;
+                s[v] = ok ? s[v] : -INFINITY;
+            }
+        }
+        // P into s, dS into dp
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 d4 = *reinterpret_cast<const float4*>(db_ + r0 + 8 * j + 4 * hh);
+            const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int v = 4 * j + i;
+                s[v] = __builtin_amdgcn_exp2f(s[v]);
+                dp[v] = s[v] * (dp[v] - dl[i]);
+            }
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS; k step c covers rows r0 + 16c ..
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const bf16x8 pb = pack8(s, c);
+            const bf16x8 dsb = pack8(dp, c);
+#pragma unroll
+            for (int d = 0; d < DB; ++d) {
+                dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_op<D>(ob, r0 + 16 * c, d, lane), pb, dv[d], 0, 0, 0);
+                dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_op<D>(qb, r0 + 16 * c, d, lane), dsb, dk[d], 0, 0, 0);
+            }
+        }
+    };
+
+    auto compute = [&](int s, const unsigned char* qb, const unsigned char* ob, const float* lb, const float* db_)
+        __attribute__((always_inline)) {
+        if (!wave_keys) return;
+        const int hidx = s / nt;
+        const int t = tq0 + s - hidx * nt;
+#pragma unroll
+        for (int x = 0; x < BM / 32; ++x) {
+            const int qa = t * BM + 32 * x;
+            if (qa >= Sq) break;
+            const int pa = qa + off, pe = min(qa + 31, Sq - 1) + off;
+            const bool any = (!causal || kw0 <= pe) && (window == 0 || kw1 > pa - window);
+            if (!any) continue;
+            const bool full = (qa + 31 < Sq) && (kw0 + 31 < Sk) && (!causal || kw0 + 31 <= pa) &&
+                              (window == 0 || kw0 > pe - window);
+            block(qb, ob, lb, db_, 32 * x, qa, !full);
+        }
+    };
+
+    auto step = [&](int s, unsigned char* qc, unsigned char* oc, float* lc, float* dc, unsigned char* qn,
+                    unsigned char* on, float* ln_, float* dn) __attribute__((always_inline)) {
+        if (s + 1 < nsteps) issue(s + 1, qn, on, ln_, dn);
+        compute(s, qc, oc, lc, dc);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+
+    if (nsteps > 0) {
+        issue(0, q_lds0, o_lds0, l_lds0, d_lds0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        for (int s = 0; s < nsteps; s += 2) {
+            step(s, q_lds0, o_lds0, l_lds0, d_lds0, q_lds1, o_lds1, l_lds1, d_lds1);
+            if (s + 1 < nsteps) step(s + 1, q_lds1, o_lds1, l_lds1, d_lds1, q_lds0, o_lds0, l_lds0, d_lds0);
+        }
+    }
+
+    // accumulator value v of block db holds d = 32 db + 8(v/4) + 4hh + v%4
+    if (!key_ok) return;
+    uint16_t* kout = dK + kv_base + (size_t)key * D;
+    uint16_t* vout = dV + kv_base + (size_t)key * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int d = 32 * db + 8 * r + 4 * hh;
+            *reinterpret_cast<uint2*>(kout + d) = pack4(dk[db][4 * r] * scale, dk[db][4 * r + 1] * scale,
+                                                        dk[db][4 * r + 2] * scale, dk[db][4 * r + 3] * scale);
+            *reinterpret_cast<uint2*>(vout + d) =
+                pack4(dv[db][4 * r], dv[db][4 * r + 1], dv[db][4 * r + 2], dv[db][4 * r + 3]);
+        }
+}
+
+template <int D>
+hipError_t launch_d(const BackwardArgs& a, hipStream_t stream) {
+    const float c2 = a.scale * kLog2e;
+    if (a.Sq > 0) {
+        const int nqt = (a.Sq + kRows - 1) / kRows;
+        const long long nitems = (long long)a.B * a.Hq * nqt;
+        const long long per_xcd = (nitems + kXcds - 1) / kXcds;
+        const long long grid = per_xcd * kXcds;
+        if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o,
+                           (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.Hq, a.Hkv, a.Sq, a.Sk,
+                           a.scale, c2, a.causal, a.window, nqt, (int)nitems, (int)per_xcd);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int nkt = (a.Sk + kRows - 1) / kRows;
+    const long long nitems = (long long)a.B * a.Hkv * nkt;
+    const long long per_xcd = (nitems + kXcds - 1) / kXcds;
+    const long long grid = per_xcd * kXcds;
+    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
+                       a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.Hq, a.Hkv, a.Sq, a.Sk, a.scale, c2,
+                       a.causal, a.window, nkt, (int)nitems, (int)per_xcd);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
+    return a.D == 128 ? launch_d<128>(a, stream) : launch_d<64>(a, stream);
+}
+
+}  // namespace attn

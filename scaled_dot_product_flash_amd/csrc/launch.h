@@ -48,6 +48,22 @@ struct AppendArgs {
     int B, Hkv, D, page_size;
 };
 
+struct BackwardArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    const float* lse;   // [B, Hq, Sq] natural-log log-sum-exp from the forward pass
+    void* dq;
+    void* dk;
+    void* dv;
+    int B, Hq, Hkv, Sq, Sk, D;
+    float scale;
+    int causal, window;
+    float* delta;       // workspace, B * Hq * Sq floats (rowsum(dO * O))
+};
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 
@@ -57,5 +73,6 @@ int decode_nsplit(int B, int Hq, int Hkv, int num_cu);
 size_t decode_workspace_floats(int B, int Hq, int D, int nsplit);
 hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 
 }  // namespace attn

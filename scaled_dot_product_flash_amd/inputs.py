@@ -7,7 +7,7 @@ path and the float64 oracle consume exactly the tensors it returns.
 Recipe: a CPU ``torch.Generator`` seeded per workload draws float32 N(0, 1)
 values (the pages' workloads are random tensors too), which are rounded to
 bfloat16 with round-to-nearest-even when the workload is bf16. Draw order is
-Q, K, V for prefill; lengths, page permutation, Q, K pool, V pool for decode.
+Q, K, V for prefill (then dO for the backward pass); lengths, page permutation, Q, K pool, V pool for decode.
 """
 
 import math
@@ -28,6 +28,9 @@ WORKLOADS = {
                         dtype="bf16", causal=True, window=4096, seed=127),
     # chunked prefill: 512 new tokens per sequence against paged caches of
     # 2048..6144 tokens (the new ones included)
+    # backward pass on the causal GQA prefill shape; dO is the fourth draw
+    "gqa_causal_4k_bwd": dict(kind="backward", B=4, Hq=32, Hkv=8, Sq=4096, Sk=4096, D=128,
+                              dtype="bf16", causal=True, window=0, seed=129),
     "chunked_prefill_paged": dict(kind="paged_prefill", nseq=8, Sq=512, Hq=32, Hkv=8, D=128, page_size=16,
                                   len_lo=2048, len_hi=6144, dtype="bf16", seed=128),
 }
@@ -45,6 +48,17 @@ def prefill_inputs(B, Hq, Hkv, Sq, Sk, D, dtype="bf16", seed=0):
     k = torch.randn((B, Hkv, Sk, D), generator=g, dtype=torch.float32).to(td)
     v = torch.randn((B, Hkv, Sk, D), generator=g, dtype=torch.float32).to(td)
     return q, k, v
+
+
+def backward_inputs(B, Hq, Hkv, Sq, Sk, D, seed=0):
+    """q, k, v as prefill_inputs (bf16) plus an upstream gradient do
+    [B,Hq,Sq,D], i.i.d. N(0,1) drawn after them from the same generator."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q = torch.randn((B, Hq, Sq, D), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, Sk, D), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, Sk, D), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    do = torch.randn((B, Hq, Sq, D), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    return q, k, v, do
 
 
 def page_counts(seq_lens, page_size):
@@ -103,6 +117,8 @@ def workload_inputs(name):
     if w["kind"] == "paged_prefill":
         return paged_prefill_inputs(w["nseq"], w["Sq"], w["Hq"], w["Hkv"], w["D"], w["page_size"],
                                     w["len_lo"], w["len_hi"], w["dtype"], w["seed"])
+    if w["kind"] == "backward":
+        return backward_inputs(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Sk"], w["D"], w["seed"])
     if w["kind"] == "prefill":
         return prefill_inputs(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Sk"], w["D"],
                               w["dtype"], w["seed"])

@@ -40,7 +40,7 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared() == ["attn_decode_paged", "attn_decode_paged_window", "attn_fwd", "attn_fwd_f32",
+    assert _declared() == ["attn_bwd", "attn_decode_paged", "attn_decode_paged_window", "attn_fwd", "attn_fwd_f32",
                            "attn_fwd_f32_lse", "attn_fwd_lse", "attn_fwd_paged", "attn_kv_append", "attn_pages_create", "attn_pages_destroy", "attn_pages_free_count",
                            "attn_pages_resize", "attn_pages_table", "attn_release", "attn_strerror"]
     assert _codes() == {"ATTN_OK": OK, "ATTN_ERR_NULL": NULL, "ATTN_ERR_SHAPE": SHAPE, "ATTN_ERR_HEADS": HEADS,
@@ -160,6 +160,7 @@ def test_ctypes_signature_matches_header(lib):
     assert len(lib.attn_decode_paged.argtypes) == 13
     assert len(lib.attn_decode_paged_window.argtypes) == 14
     assert len(lib.attn_fwd_lse.argtypes) == len(lib.attn_fwd_f32_lse.argtypes) == 15
+    assert len(lib.attn_bwd.argtypes) == 19
 
 
 def _app(lib, kn=A, vn=A, kp=A, vp=A, pt=A, sl=A, B=2, Hkv=2, D=128, ps=16):
@@ -249,3 +250,33 @@ def test_fwd_paged_validation(lib, kwargs, code):
 def test_fwd_paged_empty_calls(lib):
     assert _fwdp(lib, q=None, kp=None, vp=None, pt=None, sl=None, o=None, B=0) == OK
     assert _fwdp(lib, q=None, kp=None, vp=None, pt=None, sl=None, o=None, Sq=0) == OK
+
+
+def _bwd(lib, q=A, k=A, v=A, o=A, do=A, lse=A, dq=A, dk=A, dv=A, B=1, Hq=4, Hkv=2, Sq=8, Sk=8, D=128, scale=0.1,
+         causal=1, window=0):
+    return lib.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(o=None), NULL), (dict(do=None), NULL),
+    (dict(lse=None), NULL), (dict(dq=None), NULL), (dict(dk=None), NULL), (dict(dv=None), NULL),
+    (dict(B=-1), SHAPE), (dict(Sq=-1), SHAPE), (dict(Sk=-1), SHAPE), (dict(Sk=0), SHAPE),
+    (dict(Sq=9, Sk=8), SHAPE), (dict(Sk=1 << 23), SHAPE), (dict(Sq=1 << 23, Sk=1 << 23, causal=0), SHAPE),
+    (dict(Hq=0), HEADS), (dict(Hkv=3), HEADS), (dict(D=96), HEADDIM),
+    (dict(causal=2), MASK), (dict(causal=0, window=4), MASK), (dict(window=-1), MASK),
+    (dict(scale=float("inf")), SCALE),
+    (dict(q=U), ALIGN), (dict(k=U), ALIGN), (dict(v=U), ALIGN), (dict(o=U), ALIGN), (dict(do=U), ALIGN),
+    (dict(lse=A + 2), ALIGN), (dict(dq=U), ALIGN), (dict(dk=U), ALIGN), (dict(dv=U), ALIGN),
+])
+def test_bwd_validation(lib, kwargs, code):
+    assert _bwd(lib, **kwargs) == code
+
+
+def test_bwd_empty_calls(lib):
+    none = dict(q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None)
+    assert _bwd(lib, B=0, **none) == OK
+    assert _bwd(lib, Sq=0, Sk=0, causal=0, **none) == OK
+    # Sq = 0 with keys still owes zero dk, dv: those two pointers are required
+    assert _bwd(lib, Sq=0, **none) == NULL
+    assert _bwd(lib, Sq=0, **dict(none, dk=A)) == NULL
+    assert _bwd(lib, Sq=0, **dict(none, dk=A, dv=U)) == ALIGN
