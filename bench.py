@@ -16,7 +16,8 @@ min(len, 4096) most recent tokens of each sequence; ``prefill_lse`` times the
 prefill that also returns each row's log-sum-exp; ``prefill_paged`` times a
 chunked prefill (512 new tokens per sequence) against a paged cache;
 ``kv_append`` times the
-append of one new token per sequence to the same cache. ``cpu_baseline`` times the
+append of one new token per sequence to the same cache; ``backward`` times the
+backward pass (dQ, dK, dV) on the prefill shape at 10·D flop per visible pair. ``cpu_baseline`` times the
 float64 oracle on a bounded sample of the prefill workload on the host cores.
 Progress goes to stderr.
 """
@@ -247,6 +248,24 @@ def main():
     torch.cuda.synchronize()
     app_ms = [e[0].elapsed_time(e[1]) for e in ev]
 
+    # backward pass on the prefill shape (outside the timed steps): attn_bwd
+    # from q, k, v, o, dO and the forward's lse
+    wb = inputs.WORKLOADS["gqa_causal_4k_bwd"]
+    bq, bk, bv, bdo = (t.to(dev) for t in inputs.workload_inputs("gqa_causal_4k_bwd"))
+    bo, blse = attn.fwd_lse(bq, bk, bv, causal=True)
+    bdq, bdk, bdv = torch.empty_like(bq), torch.empty_like(bk), torch.empty_like(bv)
+    for _ in range(args.warmup):
+        attn.bwd(bq, bk, bv, bo, bdo, blse, causal=True, dq=bdq, dk=bdk, dv=bdv)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record()
+        attn.bwd(bq, bk, bv, bo, bdo, blse, causal=True, dq=bdq, dk=bdk, dv=bdv)
+        e[1].record()
+    torch.cuda.synchronize()
+    bwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    assert all(torch.isfinite(t.float()).all() for t in (bdq, bdk, bdv))
+    del bq, bk, bv, bdo, bo, blse, bdq, bdk, bdv
+
     import statistics
 
     p_flops = work.prefill_flops(wp["B"], wp["Hq"], wp["Sq"], wp["Sk"], wp["D"], True, 0)
@@ -333,6 +352,18 @@ def main():
         "us_median": round(a_med * 1e3, 2), "us_mean": round(statistics.fmean(app_ms) * 1e3, 2),
         "bytes_per_call": a_bytes, "GBps": round(a_bytes / (a_med * 1e-3) / 1e9, 2),
         "note": "latency-bound: a few KiB per sequence, one workgroup per sequence",
+    }
+    b_flops = work.backward_flops(wb["B"], wb["Hq"], wb["Sq"], wb["Sk"], wb["D"], True, 0)
+    b_mean = statistics.fmean(bwd_ms)
+    b_tflops = b_flops / (b_mean * 1e-3) / 1e12
+    out["backward"] = {
+        "workload": f"backward of the causal GQA prefill: B={wb['B']} Sq=Sk={wb['Sq']} Hq={wb['Hq']} "
+                    f"Hkv={wb['Hkv']} D={wb['D']}",
+        "flop_per_call": b_flops, "flop_convention": "10*D per visible pair (2.5x the forward)",
+        "ms_mean": round(b_mean, 5), "ms_median": round(statistics.median(bwd_ms), 5),
+        "ms_min": round(min(bwd_ms), 5), "tflops": round(b_tflops, 3),
+        "frac_peak": round(b_tflops / PEAK_BF16_TFLOPS, 4),
+        "kernels": "bwd_dq_kernel then bwd_dkdv_kernel; scores and dP are computed in both (14*D executed)",
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline (~{args.cpu_seconds:.0f} s of oracle work)")

@@ -16,31 +16,31 @@
 //
 // Two kernels run in order on the caller's stream:
 //  * bwd_dq_kernel, one workgroup per (batch, query head, 128 query rows),
-//    four waves of 32 rows. It forms Delta for its rows from dO and O (and
-//    stores it for the second kernel), keeps its Q and dO rows in registers,
-//    and streams 64-key tiles of K and V through LDS as the forward pass
-//    does: S^T = K Q^T and dP^T = V dO^T on MFMA (a lane owns one query),
-//    then dS, then dQ^T += K^T dS^T with the K^T operand read by the
-//    transposing LDS read.
-//  * bwd_dkdv_kernel, one workgroup per (batch, kv head, 128 keys), four
-//    waves of 32 keys. Its K and V rows stay in registers; it streams 64-row
-//    tiles of Q, dO, lse and Delta of every query head of the group through
-//    LDS: S = Q K^T and dP = dO V^T (a lane owns one key), P, dS, then
-//    dV^T += dO^T P and dK^T += Q^T dS with the transposed operands read by
-//    the transposing LDS read. Summing the group's heads inside one
-//    workgroup makes dK and dV plain stores, with no atomics.
+//    four waves of 32 rows. It forms Delta and lse * log2(e) for its rows
+//    (stored for the second kernel), keeps its Q and dO rows in registers and
+//    also writes them transposed to the workspace, then streams 64-key tiles
+//    of K and V through LDS as the forward pass does: S^T = K Q^T and
+//    dP^T = V dO^T on MFMA (a lane owns one query), then dS, then
+//    dQ^T += K^T dS^T with the K^T operand read by the transposing LDS read.
+//  * bwd_dkdv_kernel, one workgroup per (batch, kv head, 256 keys), eight
+//    waves of 32 keys (a lane owns one key). K rows stay in registers and the
+//    workgroup's V rows in LDS; it streams 32-row steps of Q, dO, their
+//    transposed copies, lse and Delta for every query head of the group:
+//    S = Q K^T and dP = dO V^T, P, dS, then dV^T += dO^T P and dK^T += Q^T dS.
+//    Every MFMA operand is a plain 16-byte LDS read. Summing the group's
+//    heads inside one workgroup makes dK and dV plain stores, with no atomics.
 //
 // Both kernels take the 32x32x16 bf16 MFMA. Tiles are staged by buffer->LDS
 // DMA (rows past the end of a slice read as zeros through the buffer range
 // check), double buffered. 16-byte chunks of a tile row are XOR-swizzled so
-// that both reads of a tile, 32 rows at one chunk (row operand) and 4 rows x
-// 16 columns per 16 lanes (transposing read), avoid bank conflicts. Waves
-// skip 32x32 blocks with no visible pair; only blocks that straddle a mask
-// boundary or a tail evaluate the mask.
+// that the MFMA operand reads avoid bank conflicts. Waves skip 32x32 blocks
+// with no visible pair; only blocks that straddle a mask boundary or a tail
+// evaluate the mask.
 
 #include "launch.h"
 
 #include <cmath>
+#include <type_traits>
 
 namespace attn {
 namespace {
@@ -81,6 +81,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int byt
 //    two adjacent chunks each; the swizzle sends the four rows' chunk pairs
 //    to four different pairs (D = 128: bits 1-2 carry row & 3; D = 64: rows
 //    r0, r0+2 share a parity and differ in bit 1).
+// Measured on the dQ kernel: a variant that also keeps the two 16-lane
+// halves of a transposing read apart (bits 2-3 = row & 3) counts 16x fewer
+// bank-conflict cycles but runs about 20 % slower, so this one stays.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
     if constexpr (D == 128) return ((row & 3) << 1) | ((row >> 2) & 1) | (row & 8);
@@ -158,8 +161,10 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2)
 void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
-                   float* __restrict__ Delta, uint16_t* __restrict__ dQ, int Hq, int Hkv, int Sq, int Sk,
-                   float scale, float c2, int causal, int window, int nqt, int nitems, int per_xcd) {
+                   float* __restrict__ Delta, float* __restrict__ L2, uint16_t* __restrict__ dQ,
+                   uint16_t* __restrict__ QT,
+                   uint16_t* __restrict__ dOT, int Hq, int Hkv, int Sq, int Sk, float scale, float c2, int causal,
+                   int window, int nqt, int nitems, int per_xcd, int nqb) {
     constexpr int BN = kTile, KB = BN / 32, DS = D / 16, DB = D / 32;
     constexpr int TILE_BYTES = BN * D * 2;
     __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILE_BYTES];
@@ -230,10 +235,42 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
             for (int e = 0; e < 8; ++e) dsum = fmaf((float)doreg[s][e], (float)ob[e], dsum);
         }
     }
+    // Transposed copies of this wave's 32 rows of Q and dO for the dK/dV
+    // kernel: one [D][32] bf16 block per (batch, head, 32-row block), the rows
+    // of each 16-row group stored in the order 0-3, 8-11, 4-7, 12-15, the
+    // order in which a 32x32 accumulator hands a lane its rows, so that a
+    // lane there reads its 8 operand values as one 16-byte chunk. The rows go
+    // through this wave's 8 KiB of the first K/V tile buffers and come back
+    // transposed by the transposing LDS read.
+    if (wave_rows) {
+        unsigned char* scr = (wave < 2 ? k_lds0 : k_lds1) + (wave & 1) * (32 * D * 2);
+        const size_t blk = (((size_t)b * Hq + h) * nqb + (wr0 >> 5)) * (size_t)(32 * D);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            uint16_t* dst = (m == 0 ? QT : dOT) + blk;
+#pragma unroll
+            for (int st = 0; st < DS; ++st)
+                *reinterpret_cast<uint4*>(scr + ln * (D * 2) + (((2 * st + hh) ^ swz<D>(ln)) << 4)) =
+                    __builtin_bit_cast(uint4, m == 0 ? qreg[st] : doreg[st]);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    *reinterpret_cast<uint4*>(dst + (32 * db + ln) * 32 + 16 * c + 8 * hh) =
+                        __builtin_bit_cast(uint4, tr_op<D>(scr, 16 * c, db, lane));
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+    }
+    __syncthreads();  // the scratch is reused by the first K/V tile
+
     const float delta = dsum + __shfl_xor(dsum, 32);
     const size_t row_idx = ((size_t)b * Hq + h) * Sq + qrow;
-    if (row_ok && hh == 0) Delta[row_idx] = delta;
     const float lse2 = row_ok ? LSE[row_idx] * kLog2e : 0.f;
+    if (row_ok && hh == 0) {
+        Delta[row_idx] = delta;
+        L2[row_idx] = lse2;  // lse in log2 units, for the dK/dV kernel
+    }
 
     f32x16 dq[DB];
 #pragma unroll
@@ -330,33 +367,95 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // dK, dV
 
+constexpr int kKvWaves = 8;               // waves per dK/dV workgroup
+constexpr int kKvKeys = 32 * kKvWaves;    // keys per dK/dV workgroup
+constexpr int kQB = 32;                   // query rows per streamed step
+
+// Chunk swizzle of a transposed [D][32] block in LDS: rows of 64 bytes, four
+// to a 256-byte bank line; 16 lanes reading rows d .. d+15 at one chunk hit
+// 16 different 16-byte bank groups.
+__device__ __forceinline__ int tswz(int d) { return (d >> 2) & 3; }
+
+// MFMA operand from a transposed block: row d (one column of the tile),
+// 16-byte chunk `chunk` (8 stored rows).
+__device__ __forceinline__ bf16x8 t_op(const unsigned char* t, int d, int chunk) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(t + d * 64 + ((chunk ^ tswz(d)) << 4)));
+}
+
+// Stage `ROWS` rows (from r_first) of a [rows, D] bf16 slice, row-swizzled as
+// dma_tile does, spread over NW waves.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, int r_first, unsigned char* dst, int wave,
+                                         int lane) {
+    constexpr int CPR = D / 8, RPS = 64 / CPR, SLOTS = ROWS * D * 2 / 1024;
+    static_assert(SLOTS % NW == 0 || SLOTS < NW, "DMA slots per wave");
+#pragma unroll
+    for (int i = 0; i < (SLOTS + NW - 1) / NW; ++i) {
+        const int sl = wave + NW * i;
+        if (SLOTS < NW && sl >= SLOTS) break;
+        const int row = sl * RPS + lane / CPR;
+        const int chunk = (lane % CPR) ^ swz<D>(row);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + sl * 1024), 16,
+                                                 (unsigned)(((r_first + row) * D + 8 * chunk) * 2), 0, 0, 0);
+    }
+}
+
+// Stage one transposed [D][32] block (D * 64 contiguous bytes from byte
+// offset `src`) with the tswz chunk swizzle.
+template <int D, int NW>
+__device__ __forceinline__ void dma_tblock(__amdgpu_buffer_rsrc_t rs, unsigned src, unsigned char* dst, int wave,
+                                           int lane) {
+    constexpr int SLOTS = D * 64 / 1024;
+    static_assert(SLOTS <= NW, "one DMA slot per wave at most");
+    if (wave < SLOTS) {
+        const int row = 16 * wave + (lane >> 2);
+        const int chunk = (lane & 3) ^ tswz(row);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + wave * 1024), 16,
+                                                 src + (unsigned)(row * 64 + chunk * 16), 0, 0, 0);
+    }
+}
+
+// One workgroup per (batch, kv head, 256 keys), eight waves of 32 keys. A
+// lane owns one key: its K row is the register B operand of S = Q K^T and its
+// V row, read from the workgroup's V block in LDS, that of dP = dO V^T. Each
+// step streams 32 query rows of one query head: Q and dO rows (row operands
+// of S and dP), their transposed blocks (operands of dV^T += dO^T P and
+// dK^T += Q^T dS, plain 16-byte reads), lse (log2 units) and Delta.
+//
+// Steps walk the query tiles from the last one down, all heads of the group
+// per tile, so the workgroups of one (batch, kv head) that run together read
+// the same tiles at about the same time. Workgroups are dispatched key block
+// major: under a causal mask the first key blocks carry the most work and go
+// first, and with (batch, kv head) = blockIdx % (B * Hkv) one (batch, kv head)
+// stays on one XCD when B * Hkv is a multiple of 8.
 template <int D>
-__global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2)
+__global__ __launch_bounds__(64 * kKvWaves, 1)
 void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                     const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dK,
+                     const uint16_t* __restrict__ QT, const uint16_t* __restrict__ dOT,
+                     const float* __restrict__ L2, const float* __restrict__ Delta, uint16_t* __restrict__ dK,
                      uint16_t* __restrict__ dV, int Hq, int Hkv, int Sq, int Sk, float scale, float c2, int causal,
-                     int window, int nkt, int nitems, int per_xcd) {
-    constexpr int BM = kTile, DS = D / 16, DB = D / 32;
-    constexpr int TILE_BYTES = BM * D * 2;
-    __shared__ __attribute__((aligned(16))) unsigned char q_lds0[TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char q_lds1[TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char o_lds0[TILE_BYTES];  // dO
-    __shared__ __attribute__((aligned(16))) unsigned char o_lds1[TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) float l_lds0[BM];                    // lse
-    __shared__ __attribute__((aligned(16))) float l_lds1[BM];
-    __shared__ __attribute__((aligned(16))) float d_lds0[BM];                    // Delta
-    __shared__ __attribute__((aligned(16))) float d_lds1[BM];
+                     int window, int nqb, int nbg) {
+    constexpr int NW = kKvWaves, DS = D / 16, DB = D / 32, NP = 2 * DB;
+    constexpr int RT = kQB * D * 2;   // bytes of a row tile and of a transposed block
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds[kKvKeys * D * 2];
+    __shared__ __attribute__((aligned(16))) unsigned char q_lds0[RT];
+    __shared__ __attribute__((aligned(16))) unsigned char q_lds1[RT];
+    __shared__ __attribute__((aligned(16))) unsigned char o_lds0[RT];    // dO rows
+    __shared__ __attribute__((aligned(16))) unsigned char o_lds1[RT];
+    __shared__ __attribute__((aligned(16))) unsigned char qt_lds0[RT];   // Q^T blocks
+    __shared__ __attribute__((aligned(16))) unsigned char qt_lds1[RT];
+    __shared__ __attribute__((aligned(16))) unsigned char ot_lds0[RT];   // dO^T blocks
+    __shared__ __attribute__((aligned(16))) unsigned char ot_lds1[RT];
+    __shared__ __attribute__((aligned(16))) float l_lds0[64];            // lse, log2 units (32 used)
+    __shared__ __attribute__((aligned(16))) float l_lds1[64];
+    __shared__ __attribute__((aligned(16))) float d_lds0[64];            // Delta
+    __shared__ __attribute__((aligned(16))) float d_lds1[64];
 
-    // work item: (batch, kv head) major, key block ascending (under a causal
-    // mask the first keys are seen by the most queries); each XCD takes a
-    // contiguous run, so the key blocks of one head share Q and dO in its L2
     const int w = blockIdx.x;
-    const int item = (w % kXcds) * per_xcd + w / kXcds;
-    if (item >= nitems) return;
+    const int kt = w / nbg;
+    const int bg = w % nbg;
     const int G = Hq / Hkv;
-    const int kt = item % nkt;
-    const int bg = item / nkt;
     const int g = bg % Hkv;
     const int b = bg / Hkv;
 
@@ -367,33 +466,28 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const int hh = lane >> 5;
 
     const int off = Sk - Sq;
-    const int k0 = kt * kRows;
+    const int k0 = kt * kKvKeys;
     const int kw0 = k0 + 32 * wave;                 // first key of this wave
     const int kw1 = min(kw0 + 31, Sk - 1);
     const bool wave_keys = kw0 < Sk;
     const int key = kw0 + ln;
     const bool key_ok = key < Sk;
 
-    // this lane's key row: K and V as MFMA B operands
     const size_t kv_base = ((size_t)b * Hkv + g) * (size_t)Sk * D;
-    bf16x8 kreg[DS], vreg[DS];
+    bf16x8 kreg[DS];
     {
         const size_t rb = kv_base + (size_t)(key_ok ? key : 0) * D + 8 * hh;
 #pragma unroll
-        for (int s = 0; s < DS; ++s) {
-            const uint4 z = make_uint4(0, 0, 0, 0);
-            kreg[s] = as_bf16x8(key_ok ? ld_global16(K + rb + 16 * s) : z);
-            vreg[s] = as_bf16x8(key_ok ? ld_global16(V + rb + 16 * s) : z);
-        }
+        for (int s = 0; s < DS; ++s) kreg[s] = as_bf16x8(key_ok ? ld_global16(K + rb + 16 * s) : make_uint4(0, 0, 0, 0));
     }
 
     // queries that see at least one key of the workgroup: position p = q + off
     // sees key j iff j <= p (causal) and j > p - window
-    const int kmax = min(k0 + kRows, Sk) - 1;
+    const int kmax = min(k0 + kKvKeys, Sk) - 1;
     const int q_lo = causal ? max(0, k0 - off) : 0;
     const int q_hi = (causal && window > 0) ? min(Sq - 1, kmax + window - 1 - off) : Sq - 1;
-    const int tq0 = q_lo / BM;
-    const int nt = q_lo <= q_hi ? q_hi / BM - tq0 + 1 : 0;
+    const int t_hi = q_hi / kQB;
+    const int nt = q_lo <= q_hi ? t_hi - q_lo / kQB + 1 : 0;
     const int nsteps = G * nt;
 
     f32x16 dk[DB], dv[DB];
@@ -405,41 +499,86 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             dv[db][v] = 0.f;
         }
 
-    auto issue = [&](int s, unsigned char* qd, unsigned char* od, float* ld, float* dd) __attribute__((always_inline)) {
-        const int hidx = s / nt;
-        const int t = tq0 + s - hidx * nt;
-        const size_t rows = ((size_t)b * Hq + g * G + hidx) * (size_t)Sq;
-        dma_tile<D>(rsrc(Q + rows * D, Sq * D * 2), t * BM, qd, wave, lane);
-        dma_tile<D>(rsrc(dO + rows * D, Sq * D * 2), t * BM, od, wave, lane);
-        if (wave == 0)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(LSE + rows, Sq * 4), (lds_void*)ld, 4,
-                                                     (unsigned)((t * BM + lane) * 4), 0, 0, 0);
-        else if (wave == 1)
+    // step s: query tile t_hi - s / G of query head g * G + s % G
+    auto issue = [&](int s, unsigned char* qd, unsigned char* od, float* ld, float* dd, unsigned char* qtd,
+                     unsigned char* otd) __attribute__((always_inline)) {
+        const int t = t_hi - s / G;
+        const int bh = b * Hq + g * G + s % G;
+        const size_t rows = (size_t)bh * Sq;
+        const size_t blocks = (size_t)bh * nqb * (kQB * D);
+        dma_rows<D, kQB, NW>(rsrc(Q + rows * D, Sq * D * 2), t * kQB, qd, wave, lane);
+        dma_rows<D, kQB, NW>(rsrc(dO + rows * D, Sq * D * 2), t * kQB, od, wave, lane);
+        dma_tblock<D, NW>(rsrc(QT + blocks, nqb * RT), (unsigned)(t * RT), qtd, wave, lane);
+        dma_tblock<D, NW>(rsrc(dOT + blocks, nqb * RT), (unsigned)(t * RT), otd, wave, lane);
+        if (wave == NW - 1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(L2 + rows, Sq * 4), (lds_void*)ld, 4,
+                                                     (unsigned)((t * kQB + lane) * 4), 0, 0, 0);
+        else if (wave == NW - 2)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(Delta + rows, Sq * 4), (lds_void*)dd, 4,
-                                                     (unsigned)((t * BM + lane) * 4), 0, 0, 0);
+                                                     (unsigned)((t * kQB + lane) * 4), 0, 0, 0);
+    };
+    // does step s have a visible (query, key) pair for this wave; does it
+    // need the mask (a boundary or a tail crosses it)
+    auto visible_step = [&](int s, bool& edge) __attribute__((always_inline)) {
+        const int qa = (t_hi - s / G) * kQB;
+        const int pa = qa + off, pe = min(qa + kQB - 1, Sq - 1) + off;
+        const bool any = wave_keys && (!causal || kw0 <= pe) && (window == 0 || kw1 > pa - window);
+        edge = !((qa + kQB - 1 < Sq) && (kw0 + 31 < Sk) && (!causal || kw0 + 31 <= pa) &&
+                 (window == 0 || kw0 > pe - window));
+        return any;
     };
 
-    // one 32-query block at tile rows r0 .. r0+31 (queries qa .. qa+31)
-    auto block = [&](const unsigned char* qb, const unsigned char* ob, const float* lb, const float* db_,
-                     int r0, int qa, bool edge) __attribute__((always_inline)) {
-        f32x16 s, dp;
+    // LDS addresses: with 2st + hh = 2st ^ hh, chunk (2st + hh) ^ sw of a row
+    // is chunk hh ^ sw XOR 2st, so the byte offset of k step st is a per-lane
+    // base XOR (st << 5) and a tile's base is the instruction's immediate
+    // offset; row 32 d + ln of a transposed block is 2048 d bytes past row
+    // ln. The bases are made opaque at each use so the compiler recomputes
+    // the XORs instead of keeping one address register per k step.
+    const int sw = swz<D>(ln) ^ hh;
+    auto ld16 = [](const unsigned char* p) __attribute__((always_inline)) {
+        return as_bf16x8(*reinterpret_cast<const uint4*>(p));
+    };
+
+    // S and dP of one step, then P and dS packed as bf16 operands. Operands
+    // are read one k step ahead of their MFMAs, and the scheduling barriers
+    // keep the compiler from hoisting more reads than that (the register file
+    // holds K, dK and dV for the whole kernel).
+    auto forward_part = [&](const unsigned char* qb, const unsigned char* ob, const float* lb, const float* dlb,
+                            int qa, bool edge, bf16x8* pb, bf16x8* dsb) __attribute__((always_inline)) {
+        int aq = ln * (D * 2) + (sw << 4);
+        int av = (32 * wave + ln) * (D * 2) + (sw << 4);
+        asm volatile("" : "+v"(aq), "+v"(av));
+        f32x16 S, P;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            s[v] = 0.f;
-            dp[v] = 0.f;
+            S[v] = 0.f;
+            P[v] = 0.f;
         }
+        bf16x8 aqo = ld16(qb + aq), aoo = ld16(ob + aq), avo = ld16(v_lds + av);
 #pragma unroll
         for (int st = 0; st < DS; ++st) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op<D>(qb, r0 + ln, 2 * st + hh), kreg[st], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op<D>(ob, r0 + ln, 2 * st + hh), vreg[st], dp, 0, 0, 0);
+            bf16x8 nq = aqo, no = aoo, nv = avo;
+            if (st + 1 < DS) {
+                const int x = (st + 1) << 5;
+                nq = ld16(qb + (aq ^ x));
+                no = ld16(ob + (aq ^ x));
+                nv = ld16(v_lds + (av ^ x));
+            }
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqo, kreg[st], S, 0, 0, 0);
+            P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aoo, avo, P, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            aqo = nq;
+            aoo = no;
+            avo = nv;
         }
-        // accumulator value v holds query row r0 + 8(v/4) + 4hh + v%4
+        // accumulator value v holds query row 8(v/4) + 4hh + v%4 of the step;
+        // masked pairs get an exponent of -inf, so P = 0 and dS = 0 exactly
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float4 l4 = *reinterpret_cast<const float4*>(lb + r0 + 8 * j + 4 * hh);
+            const float4 l4 = *reinterpret_cast<const float4*>(lb + 8 * j + 4 * hh);
             const float l[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[4 * j + i] = fmaf(s[4 * j + i], c2, -l[i] * kLog2e);
+            for (int i = 0; i < 4; ++i) S[4 * j + i] = fmaf(S[4 * j + i], c2, -l[i]);
         }
         if (edge) {
             asm volatile("");
@@ -450,67 +589,78 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                 bool ok = q < Sq && key_ok;
                 if (causal) ok = ok && key <= p;
                 if (window > 0) ok = ok && key > p - window;
-                s[v] = ok ? s[v] : -INFINITY;
+                S[v] = ok ? S[v] : -INFINITY;
             }
         }
-        // P into s, dS into dp
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float4 d4 = *reinterpret_cast<const float4*>(db_ + r0 + 8 * j + 4 * hh);
+            const float4 d4 = *reinterpret_cast<const float4*>(dlb + 8 * j + 4 * hh);
             const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int v = 4 * j + i;
-                s[v] = __builtin_amdgcn_exp2f(s[v]);
-                dp[v] = s[v] * (dp[v] - dl[i]);
+                S[v] = __builtin_amdgcn_exp2f(S[v]);
+                P[v] = S[v] * (P[v] - dl[i]);
             }
         }
-        // dV^T += dO^T P, dK^T += Q^T dS; k step c covers rows r0 + 16c ..
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const bf16x8 pb = pack8(s, c);
-            const bf16x8 dsb = pack8(dp, c);
-#pragma unroll
-            for (int d = 0; d < DB; ++d) {
-                dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_op<D>(ob, r0 + 16 * c, d, lane), pb, dv[d], 0, 0, 0);
-                dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_op<D>(qb, r0 + 16 * c, d, lane), dsb, dk[d], 0, 0, 0);
-            }
-        }
+        pb[0] = pack8(S, 0);
+        pb[1] = pack8(S, 1);
+        dsb[0] = pack8(P, 0);
+        dsb[1] = pack8(P, 1);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    auto compute = [&](int s, const unsigned char* qb, const unsigned char* ob, const float* lb, const float* db_)
+    // dV^T += dO^T P, dK^T += Q^T dS; k step c covers the step's rows
+    // 16c .. 16c+15; operands one (c, d) pair ahead
+    auto backward_part = [&](const bf16x8* pb, const bf16x8* dsb, const unsigned char* qtb, const unsigned char* otb)
         __attribute__((always_inline)) {
-        if (!wave_keys) return;
-        const int hidx = s / nt;
-        const int t = tq0 + s - hidx * nt;
+        int at = ln * 64 + ((((ln >> 2) & 3) ^ hh) << 4);
+        asm volatile("" : "+v"(at));
+        bf16x8 to = ld16(otb + at), tq = ld16(qtb + at);
 #pragma unroll
-        for (int x = 0; x < BM / 32; ++x) {
-            const int qa = t * BM + 32 * x;
-            if (qa >= Sq) break;
-            const int pa = qa + off, pe = min(qa + 31, Sq - 1) + off;
-            const bool any = (!causal || kw0 <= pe) && (window == 0 || kw1 > pa - window);
-            if (!any) continue;
-            const bool full = (qa + 31 < Sq) && (kw0 + 31 < Sk) && (!causal || kw0 + 31 <= pa) &&
-                              (window == 0 || kw0 > pe - window);
-            block(qb, ob, lb, db_, 32 * x, qa, !full);
+        for (int x = 0; x < NP; ++x) {
+            const int c = x / DB, d = x % DB;
+            bf16x8 no = to, nq = tq;
+            if (x + 1 < NP) {
+                const int a = (at ^ (((x + 1) / DB) << 5)) + 2048 * ((x + 1) % DB);
+                no = ld16(otb + a);
+                nq = ld16(qtb + a);
+            }
+            dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to, pb[c], dv[d], 0, 0, 0);
+            dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq, dsb[c], dk[d], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            to = no;
+            tq = nq;
         }
     };
 
-    auto step = [&](int s, unsigned char* qc, unsigned char* oc, float* lc, float* dc, unsigned char* qn,
-                    unsigned char* on, float* ln_, float* dn) __attribute__((always_inline)) {
-        if (s + 1 < nsteps) issue(s + 1, qn, on, ln_, dn);
-        compute(s, qc, oc, lc, dc);
+    // step s, its tiles in the buffers of parity R (compile-time, so that
+    // every LDS address is a constant offset)
+    auto step = [&](int s, auto r2) __attribute__((always_inline)) {
+        constexpr int R = decltype(r2)::value;
+        if (s + 1 < nsteps)
+            issue(s + 1, R ? q_lds0 : q_lds1, R ? o_lds0 : o_lds1, R ? l_lds0 : l_lds1, R ? d_lds0 : d_lds1,
+                  R ? qt_lds0 : qt_lds1, R ? ot_lds0 : ot_lds1);
+        bool edge;
+        if (visible_step(s, edge)) {
+            bf16x8 pb[2], dsb[2];
+            forward_part(R ? q_lds1 : q_lds0, R ? o_lds1 : o_lds0, R ? l_lds1 : l_lds0, R ? d_lds1 : d_lds0,
+                         (t_hi - s / G) * kQB, edge, pb, dsb);
+            backward_part(pb, dsb, R ? qt_lds1 : qt_lds0, R ? ot_lds1 : ot_lds0);
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     };
 
     if (nsteps > 0) {
-        issue(0, q_lds0, o_lds0, l_lds0, d_lds0);
+        // the workgroup's V rows stay in LDS for the whole kernel
+        dma_rows<D, kKvKeys, NW>(rsrc(V + kv_base, Sk * D * 2), k0, v_lds, wave, lane);
+        issue(0, q_lds0, o_lds0, l_lds0, d_lds0, qt_lds0, ot_lds0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         for (int s = 0; s < nsteps; s += 2) {
-            step(s, q_lds0, o_lds0, l_lds0, d_lds0, q_lds1, o_lds1, l_lds1, d_lds1);
-            if (s + 1 < nsteps) step(s + 1, q_lds1, o_lds1, l_lds1, d_lds1, q_lds0, o_lds0, l_lds0, d_lds0);
+            step(s, std::integral_constant<int, 0>());
+            if (s + 1 < nsteps) step(s + 1, std::integral_constant<int, 1>());
         }
     }
 
@@ -530,9 +680,21 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         }
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 template <int D>
 hipError_t launch_d(const BackwardArgs& a, hipStream_t stream) {
     const float c2 = a.scale * kLog2e;
+    // workspace: Delta and lse in log2 units, each [B, Hq, Sq] float32, then
+    // the transposed Q and dO blocks, each [B, Hq, ceil(Sq / 32), D, 32] bf16
+    const int nqb = (a.Sq + kQB - 1) / kQB;
+    unsigned char* ws = static_cast<unsigned char*>(a.ws);
+    const size_t rbytes = align256((size_t)a.B * a.Hq * a.Sq * 4);
+    float* delta = reinterpret_cast<float*>(ws);
+    float* l2 = reinterpret_cast<float*>(ws + rbytes);
+    const size_t tbytes = (size_t)a.B * a.Hq * nqb * kQB * D * 2;
+    uint16_t* qt = reinterpret_cast<uint16_t*>(ws + 2 * rbytes);
+    uint16_t* dot = reinterpret_cast<uint16_t*>(reinterpret_cast<unsigned char*>(qt) + align256(tbytes));
     if (a.Sq > 0) {
         const int nqt = (a.Sq + kRows - 1) / kRows;
         const long long nitems = (long long)a.B * a.Hq * nqt;
@@ -541,24 +703,28 @@ hipError_t launch_d(const BackwardArgs& a, hipStream_t stream) {
         if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
         hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o,
-                           (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.Hq, a.Hkv, a.Sq, a.Sk,
-                           a.scale, c2, a.causal, a.window, nqt, (int)nitems, (int)per_xcd);
+                           (const uint16_t*)a.dout, a.lse, delta, l2, (uint16_t*)a.dq, qt, dot, a.Hq, a.Hkv, a.Sq, a.Sk,
+                           a.scale, c2, a.causal, a.window, nqt, (int)nitems, (int)per_xcd, nqb);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int nkt = (a.Sk + kRows - 1) / kRows;
-    const long long nitems = (long long)a.B * a.Hkv * nkt;
-    const long long per_xcd = (nitems + kXcds - 1) / kXcds;
-    const long long grid = per_xcd * kXcds;
+    const int nkt = (a.Sk + kKvKeys - 1) / kKvKeys;
+    const int nbg = a.B * a.Hkv;
+    const long long grid = (long long)nbg * nkt;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)grid), dim3(64 * kKvWaves), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
-                       a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.Hq, a.Hkv, a.Sq, a.Sk, a.scale, c2,
-                       a.causal, a.window, nkt, (int)nitems, (int)per_xcd);
+                       qt, dot, l2, delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.Hq, a.Hkv, a.Sq, a.Sk, a.scale, c2,
+                       a.causal, a.window, nqb, nbg);
     return hipGetLastError();
 }
 
 }  // namespace
+
+size_t backward_workspace_bytes(int B, int Hq, int Sq, int D) {
+    const size_t nqb = (size_t)(Sq + kQB - 1) / kQB;
+    return 2 * align256((size_t)B * Hq * Sq * 4) + 2 * align256((size_t)B * Hq * nqb * kQB * D * 2);
+}
 
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
     return a.D == 128 ? launch_d<128>(a, stream) : launch_d<64>(a, stream);

@@ -61,7 +61,7 @@ struct BackwardArgs {
     int B, Hq, Hkv, Sq, Sk, D;
     float scale;
     int causal, window;
-    float* delta;       // workspace, B * Hq * Sq floats (rowsum(dO * O))
+    void* ws;           // workspace of backward_workspace_bytes(B, Hq, Sq, D) bytes
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
@@ -73,6 +73,7 @@ int decode_nsplit(int B, int Hq, int Hkv, int num_cu);
 size_t decode_workspace_floats(int B, int Hq, int D, int nsplit);
 hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+size_t backward_workspace_bytes(int B, int Hq, int Sq, int D);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 
 }  // namespace attn

@@ -7,6 +7,7 @@ Conventions (pinned in ``tests/test_work_counts.py`` against the pages' tables):
   "KV cache", prints last-step FLOP counts for a 64-dim layer that equal
   6nD² + 4n²D + 2D² without a cache and 8D² + 4nD with one; the attention
   terms are 4·D per pair.
+* The backward pass costs 10·D flop per visible pair (``backward_flops``).
 * The KV cache holds 2·Hkv·D elements per token and layer (K and V), as in the
   KV-memory formulas of "LLM 核心技术：Attention 机制的实现与优化" (section
   "内存开销对比") and the per-token table of "拆开 LLM（二）" (section
@@ -48,6 +49,17 @@ def attention_flops(pairs, D):
 
 def prefill_flops(B, Hq, Sq, Sk, D, causal, window):
     return attention_flops(B * Hq * visible_pairs(Sq, Sk, causal, window), D)
+
+
+def backward_flops(B, Hq, Sq, Sk, D, causal, window):
+    """Algorithmic flop of the backward pass: 10·D per visible pair.
+
+    Five products of 2·D flop per pair: the scores recomputed from q and k,
+    dP = dO V^T, dV = P^T dO, dQ = dS K and dK = dS^T Q, i.e. 2.5 times the
+    forward count. A kernel that recomputes the scores twice does more work
+    than this; the count is the method's, not the kernels'.
+    """
+    return 10 * D * visible_pairs(Sq, Sk, causal, window) * B * Hq
 
 
 def kv_bytes_per_token(Hkv, D, elem_bytes):

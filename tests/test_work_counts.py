@@ -70,3 +70,10 @@ def test_decode_window_bytes():
     # the windowed pair count of one query at the end of n keys is min(n, W)
     for n in lens:
         assert work.visible_pairs(1, n, True, 4096) == min(n, 4096)
+
+
+def test_backward_flops_is_five_products_per_pair():
+    # five matrix products of 2·D flop per visible pair = 2.5x the forward's 4·D
+    for args in [(4, 32, 4096, 4096, 128, True, 0), (1, 2, 100, 300, 64, False, 0), (1, 4, 50, 50, 128, True, 7)]:
+        assert work.backward_flops(*args) * 2 == 5 * work.prefill_flops(*args)
+    assert work.backward_flops(1, 1, 3, 3, 2, True, 0) == 10 * 2 * 6
