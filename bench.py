@@ -17,7 +17,9 @@ prefill that also returns each row's log-sum-exp; ``prefill_paged`` times a
 chunked prefill (512 new tokens per sequence) against a paged cache;
 ``kv_append`` times the
 append of one new token per sequence to the same cache; ``backward`` times the
-backward pass (dQ, dK, dV) on the prefill shape at 10·D flop per visible pair. ``cpu_baseline`` times the
+backward pass (dQ, dK, dV) on the prefill shape at 10·D flop per visible pair;
+``other_prefill`` times the float32 128-token, GPT-2-sized causal and 16k
+sliding-window prefill configurations. ``cpu_baseline`` times the
 float64 oracle on a bounded sample of the prefill workload on the host cores.
 Progress goes to stderr.
 """
@@ -266,6 +268,38 @@ def main():
     assert all(torch.isfinite(t.float()).all() for t in (bdq, bdk, bdv))
     del bq, bk, bv, bdo, bo, blse, bdq, bdk, bdv
 
+    # the other prefill configurations (outside the timed steps): the
+    # float32 128-token case (latency), the GPT-2-sized causal case and the
+    # 16k sliding-window case, each timed back to back after a warm-up
+    def time_prefill(name, reps):
+        w = inputs.WORKLOADS[name]
+        tq, tk, tv = (t.to(dev) for t in inputs.workload_inputs(name))
+        to = torch.empty_like(tq)
+        fn = attn.fwd_f32 if w["dtype"] == "f32" else attn.fwd
+        for _ in range(reps):
+            fn(tq, tk, tv, o=to, causal=w["causal"], window=w["window"])
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for e in evs:
+            e[0].record()
+            fn(tq, tk, tv, o=to, causal=w["causal"], window=w["window"])
+            e[1].record()
+        torch.cuda.synchronize()
+        assert torch.isfinite(to.float()).all()
+        return w, [e[0].elapsed_time(e[1]) for e in evs]
+
+    other = {}
+    for name, reps in (("tiny_f32", 200), ("gpt2_causal", 200), ("swa_16k_w4k", max(args.steps, 20))):
+        w, ms = time_prefill(name, reps)
+        fl = work.prefill_flops(w["B"], w["Hq"], w["Sq"], w["Sk"], w["D"], w["causal"], w["window"])
+        med = sorted(ms)[len(ms) // 2]
+        other[name] = {
+            "shape": f"B={w['B']} Hq={w['Hq']} Hkv={w['Hkv']} Sq=Sk={w['Sq']} D={w['D']} {w['dtype']} "
+                     f"causal={w['causal']} window={w['window']}",
+            "us_median": round(med * 1e3, 2), "flop_per_call": fl,
+            "tflops": round(fl / (med * 1e-3) / 1e12, 3),
+            "frac_peak": round(fl / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4) if w["dtype"] == "bf16" else None,
+        }
+
     import statistics
 
     p_flops = work.prefill_flops(wp["B"], wp["Hq"], wp["Sq"], wp["Sk"], wp["D"], True, 0)
@@ -365,6 +399,7 @@ def main():
         "frac_peak": round(b_tflops / PEAK_BF16_TFLOPS, 4),
         "kernels": "bwd_dq_kernel then bwd_dkdv_kernel; scores and dP are computed in both (14*D executed)",
     }
+    out["other_prefill"] = other
     if not args.no_cpu_baseline:
         log(f"cpu baseline (~{args.cpu_seconds:.0f} s of oracle work)")
         out["cpu_baseline"] = cpu_baseline(q, k, v, p_scale, args.cpu_seconds)

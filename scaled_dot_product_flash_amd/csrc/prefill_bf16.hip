@@ -511,14 +511,37 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     const int ps = 1 << ps_log2;
     const unsigned pg_lane_k = (unsigned)((8 * ((lane & 15) ^ (dma_row & 15))) * 2);
     const unsigned pg_lane_v = (unsigned)((8 * ((lane & 15) ^ ((dma_row & 3) << 2))) * 2);
-    auto issue = [&](__amdgpu_buffer_rsrc_t rs, int t, unsigned char* dst, bool is_v) __attribute__((always_inline)) {
+    // paged: the page ids of the slots a wave loads in the next step are
+    // fetched one step ahead by a vector load (lane i < SPW: K slot i of tile
+    // tk; lane SPW + i: V slot i of tile tv) and taken back with readlane. A
+    // scalar load right before the DMA would stall the wave, and its wait
+    // (the counter scalar loads share with LDS reads) would also wait for
+    // the step's first K operand reads.
+    constexpr int SPW = SLOTS / NW;
+    auto page_ids = [&](int tk, int tv) __attribute__((always_inline)) {
+        int id = 0;
+        if constexpr (PAGED) {
+            if (lane < 2 * SPW) {
+                const bool v_slot = lane >= SPW;
+                const int i = v_slot ? lane - SPW : lane;
+                const int tt = v_slot ? tv : tk;
+                const int j0 = tt * BN + 4 * NW * i + 4 * wave;
+                if (tt < t_end && j0 < Sk) id = table[off_b + (j0 >> ps_log2)];
+            }
+        }
+        return id;
+    };
+    auto issue = [&](__amdgpu_buffer_rsrc_t rs, int t, unsigned char* dst, bool is_v, int pid = 0,
+                     bool have_pid = false) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < SLOTS / NW; ++i) {
             const int sl = wave + NW * i;
             if constexpr (PAGED) {
                 const int j0 = t * BN + 4 * NW * i + 4 * wave;     // first row of the slot
                 const bool any = j0 < Sk;
-                const int page = any ? table[off_b + (j0 >> ps_log2)] : 0;
+                const int page = !any ? 0
+                                 : have_pid ? __builtin_amdgcn_readlane(pid, (is_v ? SPW : 0) + i)
+                                            : table[off_b + (j0 >> ps_log2)];
                 const uint16_t* tile = (is_v ? V : K) + ((size_t)page * Hkv + g) * ((size_t)ps * D);
                 const __amdgpu_buffer_rsrc_t pr =
                     __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, any ? ps * D * 2 : 0, kRsrcWord3);
@@ -711,12 +734,14 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
 
     using T = std::integral_constant<bool, true>;
     using F = std::integral_constant<bool, false>;
+    int pid = 0;   // paged: prefetched page ids of this step's DMA
     auto step = [&](int t, const unsigned char* kb, const unsigned char* vb, unsigned char* kdst,
                     unsigned char* vdst, f32x16 (&scur)[KB], f32x16 (&snew)[KB]) __attribute__((always_inline)) {
         bf16x8 kr[4];
         kfirst(kb, kr);
-        if (t + 2 < t_end) issue(krs, t + 2, kdst, false);
-        issue(vrs, t + 1, vdst, true);
+        if (t + 2 < t_end) issue(krs, t + 2, kdst, false, pid, PAGED);
+        issue(vrs, t + 1, vdst, true, pid, PAGED);
+        if constexpr (PAGED) pid = page_ids(t + 3, t + 2);
         float mx = main_block(T{}, kb, vb, scur, snew, kr);
         if (is_edge(t + 1)) mx = edge_extreme(snew, (t + 1) * BN);
         settle(mx);
@@ -726,8 +751,8 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     // the wave's last tile u (V(u) in vb): P(u)·V(u) only
     auto last_step = [&](int u, const unsigned char* vb, unsigned char* kdst, unsigned char* vdst,
                          f32x16 (&scur)[KB]) __attribute__((always_inline)) {
-        if (u + 2 < t_end) issue(krs, u + 2, kdst, false);
-        if (u + 1 < t_end) issue(vrs, u + 1, vdst, true);
+        if (u + 2 < t_end) issue(krs, u + 2, kdst, false, pid, PAGED);
+        if (u + 1 < t_end) issue(vrs, u + 1, vdst, true, pid, PAGED);
         bf16x8 kr[4];
         main_block(F{}, k_lds0, vb, scur, scur, kr);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -752,6 +777,7 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     __syncthreads();
     if (t_begin + 1 < t_end) issue(krs, t_begin + 1, k_lds1, false);
     issue(vrs, t_begin, v_lds0, true);
+    if constexpr (PAGED) pid = page_ids(t_begin + 2, t_begin + 1);
     {
 #pragma unroll
         for (int st = 0; st < DS; ++st)
