@@ -7,11 +7,16 @@
 // but every operand and every product stays float32: no rounding of Q, K, P
 // or V to a narrower type.
 //
-// Layout: a workgroup of 256 threads owns 64 query rows; four adjacent lanes
-// share a row and split the head dimension d = part + 4x between them, so the
-// four lanes read four consecutive floats of a staged K/V row (distinct LDS
-// banks). 32-key tiles of K and V are staged through LDS; the partial dot
-// products are summed across the four lanes with two lane exchanges.
+// Layout: a workgroup of four waves owns 16 query rows; in every wave four
+// adjacent lanes share a row and split the head dimension into four
+// contiguous quarters (d = part * D/4 + x), so a lane reads its quarter of a
+// staged K/V row with 16-byte LDS reads (the rows of a wave read the same key:
+// broadcast). The four waves take every fourth 16-key tile of the row block's
+// key range, each with its own online softmax over its tiles and its own LDS
+// tiles, and their (max, sum, output) partials are merged at the end with the
+// same rescale rule; this cuts the serial chain of a row by four for short
+// sequences. The partial dot products are summed across the four lanes of a
+// row with two DPP lane exchanges.
 
 #include "launch.h"
 
@@ -21,17 +26,29 @@ namespace attn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRows = 64;
-constexpr int kBN = 32;
+constexpr int kWaves = kThreads / 64;
+constexpr int kRows = 16;   // query rows per workgroup: four lanes per row in each wave
+constexpr int kBN = 16;     // keys per staged tile of one wave
+
+// Sums over the four lanes of a row through DPP quad permutations (lane ^ 1,
+// lane ^ 2) instead of LDS-routed shuffles: a VALU operand modifier, no LDS
+// round trip per key.
+__device__ __forceinline__ float quad_xor1(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads)
 void prefill_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                         const float* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
                         int Hq, int Hkv, int Sq, int Sk, float c2, int causal, int window, int nqt) {
-    constexpr int DP = D / 4;  // dims per lane
-    __shared__ float ks[kBN][D];
-    __shared__ float vs[kBN][D];
+    constexpr int DP = D / 4;  // dims per lane: part * DP .. part * DP + DP - 1 (16-byte LDS reads)
+    // per wave: its K and V tiles; after the key loop, its (m, l, o) partials
+    __shared__ __attribute__((aligned(16))) float ks[kWaves][kBN][D];
+    __shared__ __attribute__((aligned(16))) float vs[kWaves][kBN][D];
 
     const int item = blockIdx.x;
     const int qt = item % nqt;
@@ -41,8 +58,10 @@ void prefill_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K
     const int g = h / (Hq / Hkv);
 
     const int tid = threadIdx.x;
-    const int part = tid & 3;
-    const int row = qt * kRows + (tid >> 2);
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int part = lane & 3;
+    const int row = qt * kRows + (lane >> 2);
     const int off = Sk - Sq;
     const int pos = row + off;
 
@@ -53,7 +72,7 @@ void prefill_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K
     const bool row_ok = row < Sq;
 #pragma unroll
     for (int x = 0; x < DP; ++x) {
-        q[x] = row_ok ? Q[qo_base + (size_t)row * D + part + 4 * x] : 0.f;
+        q[x] = row_ok ? Q[qo_base + (size_t)row * D + part * DP + x] : 0.f;
         o[x] = 0.f;
     }
 
@@ -62,16 +81,24 @@ void prefill_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K
     const int hi = causal ? min(Sk, row_end - 1 + off + 1) : Sk;
     const int lo = (causal && window > 0) ? max(0, i0 + off - window + 1) : 0;
 
+    // the four waves take every fourth key tile of the workgroup's range and
+    // keep their own online softmax; the partials are merged at the end
     float m_run = -INFINITY, l_run = 0.f;
-    for (int j0 = (lo / kBN) * kBN; j0 < hi; j0 += kBN) {
-        __syncthreads();
-        for (int e = tid; e < kBN * D; e += kThreads) {
+    float (*kw)[D] = ks[wave];
+    float (*vw)[D] = vs[wave];
+    for (int j0 = (lo / kBN + wave) * kBN; j0 < hi; j0 += kWaves * kBN) {
+        // this wave's tile: 64 lanes stage kBN x D floats of K and V
+        for (int e = lane * 4; e < kBN * D; e += 64 * 4) {
             const int jj = e / D, d = e % D;
             const int j = j0 + jj;
-            ks[jj][d] = (j < Sk) ? K[kv_base + (size_t)j * D + d] : 0.f;
-            vs[jj][d] = (j < Sk) ? V[kv_base + (size_t)j * D + d] : 0.f;
+            const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+            *reinterpret_cast<float4*>(&kw[jj][d]) =
+                (j < Sk) ? *reinterpret_cast<const float4*>(K + kv_base + (size_t)j * D + d) : zero;
+            *reinterpret_cast<float4*>(&vw[jj][d]) =
+                (j < Sk) ? *reinterpret_cast<const float4*>(V + kv_base + (size_t)j * D + d) : zero;
         }
-        __syncthreads();
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
         float t[kBN];
         float mt = -INFINITY;
@@ -79,9 +106,9 @@ void prefill_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K
         for (int jj = 0; jj < kBN; ++jj) {
             float s = 0.f;
 #pragma unroll
-            for (int x = 0; x < DP; ++x) s = fmaf(q[x], ks[jj][part + 4 * x], s);
-            s += __shfl_xor(s, 1);
-            s += __shfl_xor(s, 2);
+            for (int x = 0; x < DP; ++x) s = fmaf(q[x], kw[jj][part * DP + x], s);
+            s += quad_xor1(s);
+            s += quad_xor2(s);
             const int j = j0 + jj;
             bool ok = j < Sk;
             if (causal) ok = ok && j <= pos;
@@ -101,17 +128,47 @@ void prefill_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K
             const float p = exp2f(t[jj] - m_use);
             l_run += p;
 #pragma unroll
-            for (int x = 0; x < DP; ++x) o[x] = fmaf(p, vs[jj][part + 4 * x], o[x]);
+            for (int x = 0; x < DP; ++x) o[x] = fmaf(p, vw[jj][part * DP + x], o[x]);
         }
+        // the next tile overwrites this one: finish reading it first
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_wave_barrier();
     }
 
-    if (!row_ok) return;
-    const float inv = 1.f / l_run;
-    // log-sum-exp of the scaled logits, natural log (m_run in log2 units)
-    if (LSE != nullptr && part == 0)
-        LSE[((size_t)b * Hq + h) * Sq + row] = (m_run + log2f(l_run)) * 0.69314718055994531f;
+    // merge the four waves' partials (m, l, o) with the online-softmax rule:
+    // m = max m_w, l = sum 2^(m_w - m) l_w, o = sum 2^(m_w - m) o_w
+    __syncthreads();
+    float* part_o = &ks[wave][0][0];             // 16 rows x 4 lanes x DP floats
+    float* part_ml = &vs[wave][0][0];            // 16 rows x 4 lanes x 2 floats
 #pragma unroll
-    for (int x = 0; x < DP; ++x) O[qo_base + (size_t)row * D + part + 4 * x] = o[x] * inv;
+    for (int x = 0; x < DP; ++x) part_o[lane * DP + x] = o[x];
+    part_ml[lane * 2] = m_run;
+    part_ml[lane * 2 + 1] = l_run;
+    __syncthreads();
+    if (wave != 0 || !row_ok) return;
+    float mw[kWaves], m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        mw[w] = (&vs[w][0][0])[lane * 2];
+        m = fmaxf(m, mw[w]);
+    }
+    const float m_use = (m == -INFINITY) ? 0.f : m;
+    float l = 0.f;
+#pragma unroll
+    for (int x = 0; x < DP; ++x) o[x] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const float a = exp2f(mw[w] - m_use);   // 0 for a wave that saw no visible key
+        l += a * (&vs[w][0][0])[lane * 2 + 1];
+#pragma unroll
+        for (int x = 0; x < DP; ++x) o[x] = fmaf(a, (&ks[w][0][0])[lane * DP + x], o[x]);
+    }
+    const float inv = 1.f / l;
+    // log-sum-exp of the scaled logits, natural log (m in log2 units)
+    if (LSE != nullptr && part == 0)
+        LSE[((size_t)b * Hq + h) * Sq + row] = (m + log2f(l)) * 0.69314718055994531f;
+#pragma unroll
+    for (int x = 0; x < DP; ++x) O[qo_base + (size_t)row * D + part * DP + x] = o[x] * inv;
 }
 
 template <int D>
