@@ -45,6 +45,10 @@ CASES = [
     (1, 8, 2, 1024, 1024, 128, True, 0),      # several workgroups per head
     (1, 2, 1, 64, 64, 128, False, 0),         # one tile
     (1, 4, 2, 100, 700, 64, True, 50),        # D = 64 window
+    (1, 2, 1, 300, 100, 64, False, 0),        # full attention with Sq > Sk
+    (1, 8, 1, 200, 200, 128, True, 0),        # eight query heads on one K/V head
+    (2, 4, 2, 65, 65, 128, True, 17),         # one tile plus one row, window
+    (1, 2, 2, 600, 300, 128, False, 0),       # full attention, more queries than keys, MHA
 ]
 
 
