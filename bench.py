@@ -119,8 +119,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the kernels run on one GPU's "
-              "share; see the sharding note in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (its kernels run on one GPU's "
+              "share of the work). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
