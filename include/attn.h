@@ -126,7 +126,7 @@ int attn_fwd_f32_lse(const void* q, const void* k, const void* v, void* o, float
  *                 (bottom-right alignment, as in attn_fwd with Sq <= Sk).
  *   lse         : NULL, or [B, Hq, Sq] float32 receiving the log-sum-exp of
  *                 each row as in attn_fwd_lse.
- *   D must be 128 (ATTN_ERR_HEADDIM otherwise). causal / window as in
+ *   D is 64 or 128 (ATTN_ERR_HEADDIM otherwise). causal / window as in
  *   attn_fwd. Device-side preconditions: those of attn_decode_paged, and
  *   seq_lens[b] >= Sq when causal. Slots at or past seq_lens[b] are never
  *   used (they may hold NaN). Errors: those of attn_fwd and attn_decode_paged

@@ -165,7 +165,7 @@ int attn_fwd_paged(const void* q, const void* k_pool, const void* v_pool, const 
                    int page_size, float scale, int causal, int window, hipStream_t stream) {
     if (B < 0 || Sq < 0) return ATTN_ERR_SHAPE;
     if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_HEADS;
-    if (D != 128) return ATTN_ERR_HEADDIM;
+    if (D != 64 && D != 128) return ATTN_ERR_HEADDIM;
     if (page_size < 8 || page_size > 256 || (page_size & (page_size - 1)) != 0) return ATTN_ERR_PAGE;
     if (causal != 0 && causal != 1) return ATTN_ERR_MASK;
     if (window < 0 || (window > 0 && !causal)) return ATTN_ERR_MASK;

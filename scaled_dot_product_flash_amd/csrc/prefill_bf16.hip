@@ -71,12 +71,13 @@ constexpr int kRsrcWord3 = 0x00020000;
 // Lazy-rescale threshold for the reference maximum, log2 units.
 constexpr float kLazy = 8.0f;
 
-template <int D, bool NEG>
+template <int D, bool NEG, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2)
 void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
                          int Hq, int Hkv, int Sq, int Sk, float c2, int causal, int window,
-                         int nqt, int nitems, int per_xcd) {
+                         int nqt, int nitems, int per_xcd,
+                         const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int ps_log2) {
     constexpr int BN = Tile<D>::BN;
     constexpr int KB = BN / 32;           // 32-key blocks per tile
     constexpr int KS = BN / 16;           // 16-key MFMA k-steps per tile (P·V)
@@ -103,7 +104,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     const int qt = nqt - 1 - (r1 % nqt);
     const int bg = r1 / nqt;
     const int g = bg % Hkv;
-    const int b = bg / Hkv;
+    int b = bg / Hkv;
     const int h = g * G + hg;
 
     const int tid = threadIdx.x;
@@ -112,15 +113,49 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     const int ln = lane & 31;
     const int hh = lane >> 5;
 
+    // paged: as in the pipelined kernel, sequence slot b takes the sequence
+    // of b-th largest length (up to 64 * kWaves sequences), then its length
+    // and first page-table entry off_b = sum over j < b of ceil(lens[j] / ps)
+    int off_b = 0;
+    if constexpr (PAGED) {
+        const int B = nitems / (Hq * nqt);
+        if (B <= 64 * kWaves) {
+            __shared__ int sh_seq;
+            if (tid < B) {
+                const int my = lens[tid];
+                int rank = 0;
+                for (int j = 0; j < B; ++j) {
+                    const int lj = lens[j];
+                    rank += (lj > my) || (lj == my && j < tid);
+                }
+                if (rank == b) sh_seq = tid;
+            }
+            __syncthreads();
+            b = sh_seq;
+        }
+        __shared__ int sh_part[kWaves];
+        int part = 0;
+        for (int j = tid; j < b; j += kThreads) part += (lens[j] + (1 << ps_log2) - 1) >> ps_log2;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
+        if (lane == 0) sh_part[wave] = part;
+        __syncthreads();
+#pragma unroll
+        for (int x = 0; x < kWaves; ++x) off_b += sh_part[x];
+        Sk = lens[b];
+        if (Sk < 1) return;   // outside the precondition seq_lens[b] >= 1: nothing to do
+    }
+    const int ps = 1 << ps_log2;
+
     const int off = Sk - Sq;  // bottom-right causal alignment
     const int i0 = qt * kBM;
     const int row_end = min(i0 + kBM, Sq);
 
     const size_t qo_base = ((size_t)b * Hq + h) * (size_t)Sq * D;
-    const size_t kv_base = ((size_t)b * Hkv + g) * (size_t)Sk * D;
+    const size_t kv_base = PAGED ? 0 : ((size_t)b * Hkv + g) * (size_t)Sk * D;
     // Buffer resources over this (batch, kv head) slice: rows past Sk read
     // as zeros instead of outside the slice.
-    const int kv_bytes = Sk * D * 2;
+    const int kv_bytes = PAGED ? 0 : Sk * D * 2;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(K + kv_base), 0, kv_bytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(V + kv_base), 0, kv_bytes, kRsrcWord3);
 
@@ -170,10 +205,31 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             const int u = sl * 64 + lane;          // 16-byte unit of the tile
             const int row = u / CPR, phys = u % CPR;
             const int kc = phys ^ kswz(row), vcn = phys ^ vswz(row);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + sl * 1024), 16,
-                                                     (unsigned)(((j0 + row) * D + 8 * kc) * 2), 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + sl * 1024), 16,
-                                                     (unsigned)(((j0 + row) * D + 8 * vcn) * 2), 0, 0, 0);
+            if constexpr (PAGED) {
+                // the rows of a slot (64 / CPR <= 8 consecutive, starting at a
+                // multiple of that) lie in one page (page_size >= 8); the slot
+                // reads through a buffer resource over its (page, kv head)
+                // tile, and rows at or past Sk read zeros
+                const int r0 = j0 + sl * (64 / CPR);
+                const bool any = r0 < Sk;
+                const int page = any ? table[off_b + (r0 >> ps_log2)] : 0;
+                const size_t tb = ((size_t)page * Hkv + g) * ((size_t)ps * D);
+                const int bytes = any ? ps * D * 2 : 0;
+                const __amdgpu_buffer_rsrc_t pk = __builtin_amdgcn_make_buffer_rsrc((void*)(K + tb), 0, bytes, kRsrcWord3);
+                const __amdgpu_buffer_rsrc_t pv = __builtin_amdgcn_make_buffer_rsrc((void*)(V + tb), 0, bytes, kRsrcWord3);
+                const int j = j0 + row;
+                const unsigned rb = (unsigned)((j & (ps - 1)) * D * 2);
+                const bool in = j < Sk;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(pk, (lds_void*)(kdst + sl * 1024), 16,
+                                                         in ? rb + (unsigned)(16 * kc) : (unsigned)(ps * D * 2), 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(pv, (lds_void*)(vdst + sl * 1024), 16,
+                                                         in ? rb + (unsigned)(16 * vcn) : (unsigned)(ps * D * 2), 0, 0, 0);
+            } else {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + sl * 1024), 16,
+                                                         (unsigned)(((j0 + row) * D + 8 * kc) * 2), 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + sl * 1024), 16,
+                                                         (unsigned)(((j0 + row) * D + 8 * vcn) * 2), 0, 0, 0);
+            }
         }
     };
 
@@ -852,7 +908,7 @@ hipError_t launch_pipe(const PrefillArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D, bool NEG>
+template <int D, bool NEG, bool PAGED>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     const int nqt = (a.Sq + kBM - 1) / kBM;
     const long long nitems = (long long)a.B * a.Hq * nqt;
@@ -863,9 +919,12 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     // scale 0: a tiny positive factor gives bit-identical weights (all
     // exp2(0) = 1 for finite logits) and keeps masked logits at -inf
     if (c2 == 0.f) c2 = 1e-30f;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, NEG>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+    int ps_log2 = 0;
+    while ((1 << ps_log2) < a.page_size) ++ps_log2;
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, NEG, PAGED>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                       a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)per_xcd);
+                       a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)per_xcd,
+                       a.page_table, a.seq_lens, ps_log2);
     return hipGetLastError();
 }
 
@@ -877,7 +936,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     // two workgroups per CU, then 128-row ones (four waves) for balance
     const long long wg256 = (long long)a.B * a.Hq * ((a.Sq + 255) / 256);
     const bool small = wg256 < 2LL * 256;
-    if (a.page_table != nullptr) {  // paged K/V (D = 128 only, checked by the caller)
+    if (a.page_table != nullptr) {  // paged K/V
+        if (a.D == 64) return neg ? launch_t<64, true, true>(a, stream) : launch_t<64, false, true>(a, stream);
         if (small) return neg ? launch_pipe<4, true, true>(a, stream) : launch_pipe<4, false, true>(a, stream);
         return neg ? launch_pipe<8, true, true>(a, stream) : launch_pipe<8, false, true>(a, stream);
     }
@@ -885,7 +945,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
         if (small) return neg ? launch_pipe<4, true, false>(a, stream) : launch_pipe<4, false, false>(a, stream);
         return neg ? launch_pipe<8, true, false>(a, stream) : launch_pipe<8, false, false>(a, stream);
     }
-    return neg ? launch_t<64, true>(a, stream) : launch_t<64, false>(a, stream);
+    return neg ? launch_t<64, true, false>(a, stream) : launch_t<64, false, false>(a, stream);
 }
 
 }  // namespace attn

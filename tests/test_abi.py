@@ -238,7 +238,7 @@ def _fwdp(lib, q=A, kp=A, vp=A, pt=A, sl=A, o=A, lse=None, B=2, Hq=8, Hkv=2, Sq=
     (dict(q=None), NULL), (dict(kp=None), NULL), (dict(vp=None), NULL), (dict(pt=None), NULL),
     (dict(sl=None), NULL), (dict(o=None), NULL),
     (dict(B=-1), SHAPE), (dict(Sq=-1), SHAPE),
-    (dict(Hq=0), HEADS), (dict(Hq=8, Hkv=3), HEADS), (dict(D=64), HEADDIM), (dict(D=96), HEADDIM),
+    (dict(Hq=0), HEADS), (dict(Hq=8, Hkv=3), HEADS), (dict(D=32), HEADDIM), (dict(D=96), HEADDIM),
     (dict(ps=4), PAGE), (dict(ps=48), PAGE), (dict(causal=2), MASK), (dict(causal=0, window=3), MASK),
     (dict(window=-2), MASK), (dict(scale=float("nan")), SCALE),
     (dict(q=U), ALIGN), (dict(kp=U), ALIGN), (dict(o=U), ALIGN), (dict(pt=A + 2), ALIGN), (dict(lse=A + 2), ALIGN),

@@ -19,10 +19,10 @@ from gpu_util import check_bf16, cuda, f64, needs_gpu, say
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
 
-def _case(lens, Hq, Hkv, Sq, ps, seed):
-    d = inputs.decode_inputs(len(lens), Hq, Hkv, 128, ps, 0, 0, "bf16", seed=seed, seq_lens=lens)
+def _case(lens, Hq, Hkv, Sq, ps, seed, D):
+    d = inputs.decode_inputs(len(lens), Hq, Hkv, D, ps, 0, 0, "bf16", seed=seed, seq_lens=lens)
     g = torch.Generator().manual_seed(seed)
-    q = torch.randn((len(lens), Hq, Sq, 128), generator=g).to(torch.bfloat16)
+    q = torch.randn((len(lens), Hq, Sq, D), generator=g).to(torch.bfloat16)
     return q, d
 
 
@@ -33,23 +33,28 @@ def _oracle(q, d, scale, causal, window):
 
 
 CASES = [
-    # lens, Hq, Hkv, Sq, page_size, causal, window
-    ([300, 64, 129], 8, 2, 64, 16, True, 0),
-    ([1000, 700], 8, 2, 256, 16, True, 0),       # chunked prefill: Sq < len
-    ([256, 257], 4, 4, 256, 32, True, 0),        # the whole sequence is new
-    ([500, 80], 8, 1, 80, 8, True, 37),          # sliding window, MQA
-    ([200, 333, 17], 4, 2, 17, 256, False, 0),   # non-causal
-    ([4096, 2500, 3000, 1], 32, 8, 1, 16, True, 0),   # Sq = 1: a decode step
-    ([130, 5000], 16, 4, 130, 64, True, 1000),
+    # lens, Hq, Hkv, Sq, page_size, causal, window, D
+    ([300, 64, 129], 8, 2, 64, 16, True, 0, 128),
+    ([1000, 700], 8, 2, 256, 16, True, 0, 128),       # chunked prefill: Sq < len
+    ([256, 257], 4, 4, 256, 32, True, 0, 128),        # the whole sequence is new
+    ([500, 80], 8, 1, 80, 8, True, 37, 128),          # sliding window, MQA
+    ([200, 333, 17], 4, 2, 17, 256, False, 0, 128),   # non-causal
+    ([4096, 2500, 3000, 1], 32, 8, 1, 16, True, 0, 128),   # Sq = 1: a decode step
+    ([130, 5000], 16, 4, 130, 64, True, 1000, 128),
+    ([300, 64, 129], 8, 2, 64, 16, True, 0, 64),      # D = 64: the 128-row kernel
+    ([1000, 700], 12, 12, 256, 8, True, 0, 64),
+    ([500, 80], 8, 1, 80, 32, True, 37, 64),
+    ([200, 333, 17], 4, 2, 17, 256, False, 0, 64),
+    ([2000, 1], 8, 2, 1, 16, True, 0, 64),
 ]
 
 
 @pytest.mark.parametrize("case", CASES)
 def test_paged_prefill_cases(case):
-    lens, Hq, Hkv, Sq, ps, causal, window = case
+    lens, Hq, Hkv, Sq, ps, causal, window, D = case
     say(f"paged prefill {case}")
-    q, d = _case(lens, Hq, Hkv, Sq, ps, seed=sum(lens) % 997 + Sq)
-    scale = 1.0 / math.sqrt(128)
+    q, d = _case(lens, Hq, Hkv, Sq, ps, seed=sum(lens) % 997 + Sq, D=D)
+    scale = 1.0 / math.sqrt(D)
     qd, kp, vp, pt, sl = cuda(q, d["k_pool"], d["v_pool"], d["page_table"], d["seq_lens"])
     o, lse = attn.fwd_paged(qd, kp, vp, pt, sl, scale=scale, causal=causal, window=window, lse=True)
     torch.cuda.synchronize()
@@ -63,13 +68,15 @@ def test_paged_prefill_cases(case):
     assert np.abs(f64(lse.cpu()) - want_lse).max() <= 2.0 ** -8
 
 
-def test_paged_prefill_equals_contiguous_bit_exact():
+@pytest.mark.parametrize("D", [128, 64])
+def test_paged_prefill_equals_contiguous_bit_exact(D):
     # same K/V, laid out in pages or contiguously: the same arithmetic
     B, Hq, Hkv, S, ps = 2, 8, 2, 700, 16
-    q, k, v = inputs.prefill_inputs(B, Hq, Hkv, S, S, 128, "bf16", 45)
+    say(f"paged prefill bit-exact D={D}")
+    q, k, v = inputs.prefill_inputs(B, Hq, Hkv, S, S, D, "bf16", 45)
     n_pages = (S + ps - 1) // ps
     perm = torch.randperm(B * n_pages, generator=torch.Generator().manual_seed(3))
-    kp = torch.full((B * n_pages, Hkv, ps, 128), float("nan"), dtype=torch.bfloat16)
+    kp = torch.full((B * n_pages, Hkv, ps, D), float("nan"), dtype=torch.bfloat16)
     vp = kp.clone()
     for b in range(B):
         for p in range(n_pages):
