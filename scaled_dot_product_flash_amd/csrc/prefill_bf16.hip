@@ -29,12 +29,17 @@
 //  * Tiles wholly outside a wave's causal/window range are skipped; only
 //    tiles that straddle a boundary or the key tail evaluate the mask.
 //  * Work items are ordered (batch, kv head) major, then query tile from the
-//    heaviest causal tile down, then the query heads of the group; each XCD
-//    takes a contiguous run of items so the query heads sharing a K/V head
-//    meet in the same L2.
+//    heaviest causal tile down, then the query heads of the group. The item
+//    list is cut into chunks that are dealt to the XCDs in snake order
+//    (0..7, 7..0, ...) and each XCD runs its chunks in list order, so the
+//    query heads sharing a K/V head meet in the same L2. Contiguous K/V uses
+//    one chunk per XCD; a paged cache, whose sequences differ in length and
+//    are listed longest first, uses one (batch, kv head) group per chunk, so
+//    every XCD gets a like share of long and short sequences.
 
 #include "launch.h"
 
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -56,6 +61,29 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kXcds = 8;
 
+// Work item of workgroup w under the chunked snake deal (-1: no item). Slot s
+// of XCD x = w % 8 is position s % chunk of that XCD's (s / chunk)-th chunk;
+// its k-th chunk is the list's chunk 8k + x for even k and 8k + 7 - x for odd k.
+__device__ __forceinline__ int dealt_item(int w, int chunk, int nitems) {
+    const int x = w % kXcds, s = w / kXcds;
+    const int k = s / chunk;
+    const int c = kXcds * k + ((k & 1) ? kXcds - 1 - x : x);
+    const long long item = (long long)c * chunk + s % chunk;
+    return item < nitems ? (int)item : -1;
+}
+
+// Host side of the deal: the chunk size and the grid that covers every chunk.
+struct Deal {
+    long long chunk, grid;
+};
+inline Deal make_deal(long long nitems, long long group_items, bool paged) {
+    const long long per_xcd = (nitems + kXcds - 1) / kXcds;
+    const long long chunk = paged ? std::max(1LL, std::min(group_items, per_xcd)) : std::max(1LL, per_xcd);
+    const long long nchunks = (nitems + chunk - 1) / chunk;
+    const long long rounds = (nchunks + kXcds - 1) / kXcds;
+    return {chunk, rounds * kXcds * chunk};
+}
+
 template <int D> struct Tile { static constexpr int BN = (D == 128) ? 64 : 128; };
 
 __device__ __forceinline__ uint4 ld_global16(const uint16_t* p) {
@@ -76,7 +104,7 @@ __global__ __launch_bounds__(kThreads, 2)
 void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
                          int Hq, int Hkv, int Sq, int Sk, float c2, int causal, int window,
-                         int nqt, int nitems, int per_xcd,
+                         int nqt, int nitems, int chunk,
                          const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int ps_log2) {
     constexpr int BN = Tile<D>::BN;
     constexpr int KB = BN / 32;           // 32-key blocks per tile
@@ -96,8 +124,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
 
     // ---- work item -------------------------------------------------------
     const int w = blockIdx.x;
-    const int item = (w % kXcds) * per_xcd + w / kXcds;
-    if (item >= nitems) return;
+    const int item = dealt_item(w, chunk, nitems);
+    if (item < 0) return;
     const int G = Hq / Hkv;
     const int hg = item % G;
     const int r1 = item / G;
@@ -438,7 +466,7 @@ __global__ __launch_bounds__(64 * NW, 2)
 void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
                          int Hq, int Hkv, int Sq, int Sk, float c2, int causal, int window,
-                         int nqt, int nitems, int per_xcd,
+                         int nqt, int nitems, int chunk,
                          const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int ps_log2) {
     constexpr int D = 128, BN = 64, KB = 2, KS = 4, DS = 8, DB = 4, CPR = 16;
     constexpr int TILE_BYTES = BN * D * 2;
@@ -452,8 +480,8 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     __shared__ __attribute__((aligned(16))) unsigned char v_lds1[TILE_BYTES];
 
     const int w = blockIdx.x;
-    const int item = (w % kXcds) * per_xcd + w / kXcds;
-    if (item >= nitems) return;
+    const int item = dealt_item(w, chunk, nitems);
+    if (item < 0) return;
     const int G = Hq / Hkv;
     const int hg = item % G;
     const int r1 = item / G;
@@ -894,16 +922,15 @@ template <int NW, bool NEG, bool PAGED>
 hipError_t launch_pipe(const PrefillArgs& a, hipStream_t stream) {
     const int nqt = (a.Sq + 32 * NW - 1) / (32 * NW);
     const long long nitems = (long long)a.B * a.Hq * nqt;
-    const long long per_xcd = (nitems + kXcds - 1) / kXcds;
-    const long long grid = per_xcd * kXcds;
-    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    const Deal deal = make_deal(nitems, (long long)(a.Hq / a.Hkv) * nqt, PAGED);
+    if (deal.grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     float c2 = a.scale * 1.4426950408889634f;
     if (c2 == 0.f) c2 = 1e-30f;
     int ps_log2 = 0;
     while ((1 << ps_log2) < a.page_size) ++ps_log2;
-    hipLaunchKernelGGL((prefill_pipe_kernel<NW, NEG, PAGED>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
+    hipLaunchKernelGGL((prefill_pipe_kernel<NW, NEG, PAGED>), dim3((unsigned)deal.grid), dim3(64 * NW), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                       a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)per_xcd,
+                       a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)deal.chunk,
                        a.page_table, a.seq_lens, ps_log2);
     return hipGetLastError();
 }
@@ -912,18 +939,17 @@ template <int D, bool NEG, bool PAGED>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     const int nqt = (a.Sq + kBM - 1) / kBM;
     const long long nitems = (long long)a.B * a.Hq * nqt;
-    const long long per_xcd = (nitems + kXcds - 1) / kXcds;
-    const long long grid = per_xcd * kXcds;
-    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    const Deal deal = make_deal(nitems, (long long)(a.Hq / a.Hkv) * nqt, PAGED);
+    if (deal.grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     float c2 = a.scale * 1.4426950408889634f;
     // scale 0: a tiny positive factor gives bit-identical weights (all
     // exp2(0) = 1 for finite logits) and keeps masked logits at -inf
     if (c2 == 0.f) c2 = 1e-30f;
     int ps_log2 = 0;
     while ((1 << ps_log2) < a.page_size) ++ps_log2;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, NEG, PAGED>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, NEG, PAGED>), dim3((unsigned)deal.grid), dim3(kThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                       a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)per_xcd,
+                       a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)deal.chunk,
                        a.page_table, a.seq_lens, ps_log2);
     return hipGetLastError();
 }
