@@ -46,19 +46,26 @@ CASES = [
     ([500, 80], 8, 1, 80, 32, True, 37, 64),
     ([200, 333, 17], 4, 2, 17, 256, False, 0, 64),
     ([2000, 1], 8, 2, 1, 16, True, 0, 64),
+    # more (sequence, kv head) groups than XCDs: groups dealt in snake order,
+    # 15 chunks leave the second round one short
+    ([900, 50, 400, 1200, 47], 6, 3, 40, 16, True, 0, 128),
+    # more sequences than the in-kernel longest-first ranking covers (512 for
+    # the 8-wave kernel, 256 for the D = 64 kernel): slots keep batch order
+    ([int(x) for x in np.random.default_rng(7).integers(3, 71, 600)], 8, 2, 3, 8, True, 0, 128),
+    ([int(x) for x in np.random.default_rng(8).integers(3, 301, 301)], 4, 4, 3, 16, True, 5, 64),
 ]
 
 
 @pytest.mark.parametrize("case", CASES)
 def test_paged_prefill_cases(case):
     lens, Hq, Hkv, Sq, ps, causal, window, D = case
-    say(f"paged prefill {case}")
+    say(f"paged prefill {(lens if len(lens) < 8 else f'{len(lens)} seqs'), Hq, Hkv, Sq, ps, causal, window, D}")
     q, d = _case(lens, Hq, Hkv, Sq, ps, seed=sum(lens) % 997 + Sq, D=D)
     scale = 1.0 / math.sqrt(D)
     qd, kp, vp, pt, sl = cuda(q, d["k_pool"], d["v_pool"], d["page_table"], d["seq_lens"])
     o, lse = attn.fwd_paged(qd, kp, vp, pt, sl, scale=scale, causal=causal, window=window, lse=True)
     torch.cuda.synchronize()
-    check_bf16(f64(o.cpu()), _oracle(q, d, scale, causal, window), str(case))
+    check_bf16(f64(o.cpu()), _oracle(q, d, scale, causal, window), f"{len(lens)} seqs, Sq={Sq}, D={D}")
     # log-sum-exp of the same rows, bar of the bf16 path (see test_gpu_prefill)
     want_lse = np.stack([oracle.attention_lse(
         f64(q[b:b + 1]),
