@@ -84,7 +84,6 @@ inline Deal make_deal(long long nitems, long long group_items, bool paged) {
     return {chunk, rounds * kXcds * chunk};
 }
 
-template <int D> struct Tile { static constexpr int BN = (D == 128) ? 64 : 128; };
 
 __device__ __forceinline__ uint4 ld_global16(const uint16_t* p) {
     return *reinterpret_cast<const uint4*>(p);
@@ -106,7 +105,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                          int Hq, int Hkv, int Sq, int Sk, float c2, int causal, int window,
                          int nqt, int nitems, int chunk,
                          const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int ps_log2) {
-    constexpr int BN = Tile<D>::BN;
+    constexpr int BN = 64;                // keys per tile
     constexpr int KB = BN / 32;           // 32-key blocks per tile
     constexpr int KS = BN / 16;           // 16-key MFMA k-steps per tile (P·V)
     constexpr int DS = D / 16;            // 16-wide d steps (Q·K^T)

@@ -106,6 +106,9 @@ SHAPES = [
     (1, 2, 2, 60, 170, 64, True, 8),        # the same across a 128-key tile
     (2, 16, 4, 1000, 1000, 128, True, 0),
     (1, 4, 4, 1000, 1000, 64, True, 0),
+    # D = 64 over long key ranges (many 64-key tiles per row block)
+    (1, 2, 1, 300, 4400, 64, True, 0),
+    (1, 2, 2, 4200, 4200, 64, True, 1000),
     # enough 256-row tiles for the eight-wave D = 128 kernel, ragged
     (4, 32, 8, 1000, 1000, 128, True, 0),
     (4, 32, 8, 777, 900, 128, True, 100),
