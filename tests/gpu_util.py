@@ -50,6 +50,27 @@ def check_bf16(got, want, what=""):
     return mx, mean
 
 
+def check_bf16_floor(got, want, what=""):
+    """The bf16 bar above the output's own rounding floor.
+
+    Where |O| reaches 2 and more (a sharp softmax under a large |scale|
+    returns nearly one V row), rounding the exact result to bfloat16 alone
+    moves it by up to half a bf16 spacing, 2^-7 on [2, 4) and 2^-6 on [4, 8),
+    beyond the fixed 1e-2. So each element may differ from the float64 result
+    by BF16_MAX_ABS plus |bf16(want) - want|, and the mean by BF16_MEAN_ABS
+    plus the mean of that floor.
+    """
+    want = np.asarray(want, dtype=np.float64)
+    err = np.abs(np.asarray(got, dtype=np.float64) - want)
+    assert np.all(np.isfinite(err)), f"{what}: non-finite output"
+    floor = np.abs(torch.from_numpy(want).to(torch.bfloat16).double().numpy() - want)
+    excess = float((err - floor).max())
+    mean_excess = float(err.mean() - floor.mean())
+    assert excess <= BF16_MAX_ABS and mean_excess <= BF16_MEAN_ABS, \
+        f"{what}: max abs {err.max():.3e} ({excess:.3e} above the bf16 floor), mean abs {err.mean():.3e}"
+    return excess, mean_excess
+
+
 def check_f32(got, want, what=""):
     mx, _ = errors(got, want)
     assert mx <= F32_MAX_ABS, f"{what}: max abs {mx:.3e}"
