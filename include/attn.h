@@ -26,6 +26,12 @@
  *     h / (Hq / Hkv) ("Attention 机制详解" §5.2, repeat_interleave order).
  *     Hkv == Hq is plain multi-head attention, Hkv == 1 is multi-query.
  *   - A zero batch (B == 0), or Sq == 0 for prefill, is a valid empty call.
+ *   - Graph capture: a call enqueues kernels only (no memset, copy or host
+ *     synchronisation). The one allocation is the workspace of the decode and
+ *     backward calls, kept per (device, stream) and grown on demand (growing
+ *     synchronises the stream and frees the old buffer). To capture those
+ *     calls in a HIP graph, run them once on the capture stream with the
+ *     largest shapes to be captured; the graph then reuses that workspace.
  */
 #ifndef ATTN_H
 #define ATTN_H
