@@ -400,6 +400,338 @@ void decode_merge_kernel(const float* __restrict__ ws, uint16_t* __restrict__ Op
     Op[(size_t)bh * D + d] = __builtin_bit_cast(uint16_t, ob);
 }
 
+// ---- decode on the matrix cores ---------------------------------------------
+//
+// The query heads that share a K/V head form a small dense contraction with
+// the cached tokens: S^T (tokens x heads) = K Q^T and O^T (dims x heads) +=
+// V^T P^T. With up to 32 heads as the 32 columns of v_mfma_f32_32x32x16_bf16
+// the vector ALU is left with the softmax only, which keeps the step bound by
+// HBM for groups of 4 and more heads, where the vector kernel above spends
+// most of its time in dot products and lane sums.
+//  * Grid (split, kv head x head group of <= 32, sequence by length rank);
+//    a split's 32-token tiles are dealt round-robin to the four waves, each
+//    with its own online softmax; the waves merge at the end and the split's
+//    partial (m, l, o) goes to the same workspace as the vector kernel's.
+//  * K tiles go from HBM straight into registers in the MFMA operand layout
+//    (lane%32 = token, 8-dim chunks), two tiles ahead of use; V tiles go by
+//    buffer->LDS DMA into three LDS stages per wave and are read back with
+//    the transposing LDS read as the V^T operand. Page ids are scalar loads,
+//    so waiting for them never waits for the K/V loads in flight.
+//  * Every step issues the same instructions: tokens past the length are
+//    clamped to the last token for the K loads (valid memory, masked logits)
+//    and read as zeros for V (range check), and past a wave's last tile the
+//    issue is a dummy (K from the last token, which the cache holds; V from a
+//    zero-size range, no memory traffic). The compiler then counts the loads
+//    between a tile's issue and its use exactly and waits for that tile only.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer resource word 3, gfx9 family
+constexpr int kTT = 32;                  // tokens per tile
+constexpr int kStages = 3;               // tiles per wave: one in use, two in flight
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+template <int D, bool NEG>
+__global__ __launch_bounds__(kThreads, 1)
+void decode_mfma_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __restrict__ Kp,
+                        const uint16_t* __restrict__ Vp, const int32_t* __restrict__ table,
+                        const int32_t* __restrict__ lens, float* __restrict__ ws,
+                        int Hq, int Hkv, int ps_log2, int nsplit, float c2, int window) {
+    constexpr int DS = D / 16;          // k-steps of S^T = K Q^T
+    constexpr int DB = D / 32;          // 32-dim blocks of O^T
+    constexpr int KS = kTT / 16;        // k-steps of O^T += V^T P^T
+    constexpr int CPR = D / 8;          // 16-byte chunks per row
+    constexpr int RPS = 64 / CPR;       // rows per 1 KiB DMA slot
+    constexpr int VT = kTT * D * 2;     // bytes of a V tile
+    constexpr int VSLOTS = VT / 1024;
+    constexpr int OPS = DS + VSLOTS;    // vector memory instructions per tile
+    // one LDS object per stage (four waves' tiles each), so that the
+    // compiler's wait for DMA into LDS can tell the stages apart
+    __shared__ __attribute__((aligned(16))) unsigned char vl0[kWaves * VT];
+    __shared__ __attribute__((aligned(16))) unsigned char vl1[kWaves * VT];
+    __shared__ __attribute__((aligned(16))) unsigned char vl2[kWaves * VT];
+    __shared__ float sh_m[kWaves * 32];
+    __shared__ float sh_l[kWaves * 32];
+    __shared__ int sh_len[kThreads];
+    __shared__ int sh_b;
+    __shared__ int sh_red[kWaves];
+
+    const int split = blockIdx.x;
+    const int tid = threadIdx.x;
+    int b = blockIdx.z;
+    {
+        // longest sequences first: slot z of the grid takes the sequence of
+        // length rank z (ties by index)
+        const int B = gridDim.z;
+        if (B <= kThreads) {
+            if (tid < B) sh_len[tid] = lens[tid];
+            __syncthreads();
+            if (tid < B) {
+                const int my = sh_len[tid];
+                int rank = 0;
+                for (int j = 0; j < B; ++j) {
+                    const int lj = sh_len[j];
+                    rank += (lj > my) || (lj == my && j < tid);
+                }
+                if (rank == (int)blockIdx.z) sh_b = tid;
+            }
+            __syncthreads();
+            b = __builtin_amdgcn_readfirstlane(sh_b);
+        }
+    }
+    const int G = Hq / Hkv;
+    const int ngrp = (G + 31) >> 5;
+    const int g = blockIdx.y / ngrp;
+    const int hg0 = (blockIdx.y % ngrp) * 32;
+    const int GC = min(32, G - hg0);            // heads of this group
+    const int h0 = g * G + hg0;
+    const int ps = 1 << ps_log2;
+
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int ln = lane & 31;
+    const int hh = lane >> 5;
+
+    // off_b = sum_{j<b} ceil(len_j / ps), the sequence's first page-table entry
+    int part = 0;
+    for (int j = tid; j < b; j += kThreads) part += (lens[j] + ps - 1) >> ps_log2;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
+    if (lane == 0) sh_red[wave] = part;
+    __syncthreads();
+    const int off_b = __builtin_amdgcn_readfirstlane(sh_red[0] + sh_red[1] + sh_red[2] + sh_red[3]);
+    const int len = __builtin_amdgcn_readfirstlane(lens[b]);
+    const int32_t* tab = table + off_b;
+    const int last_page = (len - 1) >> ps_log2;
+
+    if (len < 1) {
+        // outside the precondition (a sequence owns no page): an empty partial,
+        // as the vector kernel leaves; no load is issued
+        for (int idx = tid; idx < GC * D; idx += kThreads) {
+            const int j = idx / D, d = idx % D;
+            const size_t unit = ((size_t)b * Hq + h0 + j) * nsplit + split;
+            ws[unit * D + d] = 0.f;
+            if (d == 0) {
+                float* ml = ws + (size_t)gridDim.z * Hq * nsplit * D;
+                ml[2 * unit] = -INFINITY;
+                ml[2 * unit + 1] = 0.f;
+            }
+        }
+        return;
+    }
+
+    // this split's tiles of the visible tokens first .. len-1; wave w takes
+    // tiles tbeg + w, tbeg + w + 4, ...
+    const int first = window > 0 ? max(0, len - window) : 0;
+    const int tl0 = first / kTT;
+    const int ntile = (len + kTT - 1) / kTT - tl0;
+    const int tbeg = tl0 + (int)((long long)ntile * split / nsplit);
+    const int tend = tl0 + (int)((long long)ntile * (split + 1) / nsplit);
+    const int nmine = tend - tbeg > wave ? (tend - tbeg - wave + kWaves - 1) / kWaves : 0;
+
+    // Q^T operand: column ln = head hg0 + ln, k-chunk = dims 16 s + 8 hh .. +7
+    bf16x8 qreg[DS];
+    {
+        const bool ok = ln < GC;
+        const uint16_t* qp = Qp + ((size_t)b * Hq + h0 + (ok ? ln : 0)) * D + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) qreg[s] = as_bf16x8(ok ? ld16(qp + 16 * s) : make_uint4(0, 0, 0, 0));
+    }
+
+    const size_t head_stride = (size_t)ps * D;          // one (page, kv head) tile
+    const size_t page_stride = (size_t)Hkv * head_stride;
+    auto vswz = [](int row) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); };
+    unsigned char* const vs0 = vl0 + wave * VT;       // this wave's V stages
+    unsigned char* const vs1 = vl1 + wave * VT;
+    unsigned char* const vs2 = vl2 + wave * VT;
+
+    // issue tile t (this wave's k-th) into stage st: K into kdst registers,
+    // V into LDS. The tile's pages are up to four consecutive table entries,
+    // read as scalars (indices clamped to the sequence's last page).
+    auto issue = [&](int t, unsigned char* vdst, uint4 (&kdst)[DS], bool dummy) __attribute__((always_inline)) {
+        const int j0 = t * kTT;
+        const int p0 = j0 >> ps_log2;
+        int pid[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pid[i] = __builtin_amdgcn_readfirstlane(tab[min(p0 + i, last_page)]);
+        auto pick = [&](int idx) __attribute__((always_inline)) {
+            return idx == 0 ? pid[0] : idx == 1 ? pid[1] : idx == 2 ? pid[2] : pid[3];
+        };
+        // K: lane's token j0 + ln (clamped to len - 1), dims 16 s + 8 hh; a
+        // dummy reads the last token's row (valid, and cached after the first)
+        const int tok = dummy ? len - 1 : min(j0 + ln, len - 1);
+        const int page = dummy ? __builtin_amdgcn_readfirstlane(tab[last_page])
+                               : pick(min(max((tok >> ps_log2) - p0, 0), 3));
+        const uint16_t* kp = Kp + (size_t)page * page_stride + (size_t)g * head_stride +
+                             (size_t)(tok & (ps - 1)) * D + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) kdst[s] = ld16_nt(kp + 16 * s);
+        // V: slot sl holds rows sl * RPS .. +RPS-1, all in one page
+#pragma unroll
+        for (int sl = 0; sl < VSLOTS; ++sl) {
+            const int r0 = j0 + sl * RPS;
+            const bool any = !dummy && r0 < len;
+            const int vpage = pick(min(max((r0 >> ps_log2) - p0, 0), 3));
+            const uint16_t* tile = Vp + (size_t)vpage * page_stride + (size_t)g * head_stride;
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, any ? ps * D * 2 : 0, kRsrcWord3);
+            const int row = sl * RPS + lane / CPR;
+            const int j = j0 + row;
+            const int chunk = (lane % CPR) ^ vswz(row);
+            const unsigned off = j < len ? (unsigned)((j & (ps - 1)) * D * 2 + 16 * chunk) : (unsigned)(ps * D * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(vdst + sl * 1024), 16, off, 0, 0, 0);
+        }
+    };
+
+    // V^T operand: a 16-lane group reads 4 tokens x 16 dims transposed
+    const int grp = (lane >> 4) & 1;
+    const int e4 = (lane & 15) >> 2;
+    const int q4 = lane & 3;
+    auto vop = [&](const unsigned char* vb, int ks, int db) __attribute__((always_inline)) -> bf16x8 {
+        const int key0 = 16 * ks + 4 * hh + e4;
+        const int d = 32 * db + 16 * grp + 4 * q4;
+        const int o_lo = key0 * (D * 2) + (((d >> 3) ^ vswz(key0)) << 4) + ((d & 7) << 1);
+        const int o_hi = o_lo + 8 * (D * 2);     // key0 + 8: same swizzle
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + o_lo));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + o_hi));
+        const s16x8 a8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        return __builtin_bit_cast(bf16x8, a8);
+    };
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    const float masked = NEG ? INFINITY : -INFINITY;
+
+    // one tile: logits, mask at the ends of the visible range, online softmax
+    // with the lazy reference maximum, O^T += V^T P^T
+    auto compute = [&](int t, const uint4 (&kc)[DS], const unsigned char* vb) __attribute__((always_inline)) {
+        f32x16 sacc;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kc[s]), qreg[s], sacc, 0, 0, 0);
+        // accumulator value v holds token j0 + 8 (v / 4) + 4 hh + v % 4 of column ln
+        const int j0 = t * kTT;
+        if (j0 + kTT > len || j0 < first) {
+            asm volatile("");
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int j = j0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+                sacc[v] = (j < len && j >= first) ? sacc[v] : masked;
+            }
+        }
+        float mx = masked;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = NEG ? fminf(mx, sacc[v]) : fmaxf(mx, sacc[v]);
+        const float other = __shfl_xor(mx, 32);
+        mx = NEG ? fminf(mx, other) : fmaxf(mx, other);
+        const float mt = (mx == masked) ? -INFINITY : mx * c2;
+        const bool need = mt > m_run + kLazy;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
+            m_run = need ? mt : m_run;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+        }
+        const float msub = (m_run == -INFINITY) ? 0.f : m_run;
+        bf16x8 pb[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int jj = 0; jj < 8; jj += 2) {
+                const int v0 = 8 * ks + jj;
+                f32x2 pr = {__builtin_amdgcn_exp2f(fmaf(sacc[v0], c2, -msub)),
+                            __builtin_amdgcn_exp2f(fmaf(sacc[v0 + 1], c2, -msub))};
+                const bf16x2 pbf = __builtin_convertvector(pr, bf16x2);
+                l_run = __builtin_amdgcn_fdot2_f32_bf16(pbf, __builtin_bit_cast(bf16x2, kOnes), l_run, false);
+                pb[ks][jj] = pbf[0];
+                pb[ks][jj + 1] = pbf[1];
+            }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop(vb, ks, db), pb[ks], oacc[db], 0, 0, 0);
+    };
+
+    // three register sets for K, rotated with the V stages; tile k of this
+    // wave is tile tbeg + wave + 4 k
+    uint4 k0[DS], k1[DS], k2[DS];
+    issue(tbeg + wave, vs0, k0, nmine <= 0);
+    issue(tbeg + wave + kWaves, vs1, k1, nmine <= 1);
+    int k = 0;
+    auto stage_step = [&](uint4 (&kc)[DS], uint4 (&kn)[DS], const unsigned char* vc, unsigned char* vn)
+        __attribute__((always_inline)) {
+        // issue tile k + 2 into the stage tile k - 1 used, then tile k
+        issue(tbeg + wave + kWaves * (k + 2), vn, kn, k + 2 >= nmine);
+        compute(tbeg + wave + kWaves * k, kc, vc);
+        ++k;
+    };
+    while (k < nmine) {
+        stage_step(k0, k2, vs0, vs2);
+        if (k >= nmine) break;
+        stage_step(k1, k0, vs1, vs0);
+        if (k >= nmine) break;
+        stage_step(k2, k1, vs2, vs1);
+    }
+
+    // merge the waves: per head column, (m, l) and O^T rows through LDS
+    // (the V stages are free once every DMA, dummies included, has landed:
+    // waves 0, 1 use stage 0, waves 2, 3 stage 1)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    static_assert(2 * 32 * D * 4 <= kWaves * VT, "merge scratch");
+    auto sh_o = [&](int w) __attribute__((always_inline)) {
+        return reinterpret_cast<float*>(w < 2 ? vl0 : vl1) + (w & 1) * 32 * D;   // [32 heads][D]
+    };
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int d = 32 * db + 8 * (v >> 2) + 4 * hh + (v & 3);
+            sh_o(wave)[ln * D + d] = oacc[db][v];
+        }
+    if (hh == 0) {
+        sh_m[wave * 32 + ln] = m_run;
+        sh_l[wave * 32 + ln] = l_tot;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < GC * D; idx += kThreads) {
+        const int j = idx / D, d = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sh_m[w * 32 + j]);
+        const float M_use = (M == -INFINITY) ? 0.f : M;
+        float L = 0.f, acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float sc = exp2f(sh_m[w * 32 + j] - M_use);
+            L += sh_l[w * 32 + j] * sc;
+            acc += sh_o(w)[j * D + d] * sc;
+        }
+        const size_t unit = ((size_t)b * Hq + h0 + j) * nsplit + split;
+        ws[unit * D + d] = acc;
+        if (d == 0) {
+            float* ml = ws + (size_t)gridDim.z * Hq * nsplit * D;
+            ml[2 * unit] = M;
+            ml[2 * unit + 1] = L;
+        }
+    }
+}
+
 int heads_per_group(int G) {
     if (G % 8 == 0) return 8;
     if (G % 4 == 0) return 4;
@@ -416,6 +748,19 @@ void launch_split(const DecodeArgs& a, int ps_log2, float c2, hipStream_t stream
 }
 
 template <int D, bool NEG>
+void launch_mfma(const DecodeArgs& a, int ps_log2, float c2, hipStream_t stream) {
+    const int G = a.Hq / a.Hkv;
+    const int groups = a.Hkv * ((G + 31) / 32);
+    // scale 0: a tiny positive factor gives bit-identical weights (every
+    // exp2 of a finite logit is 1) and keeps masked logits at -inf instead of
+    // -inf * 0 = NaN
+    if (c2 == 0.f) c2 = 1e-30f;
+    hipLaunchKernelGGL((decode_mfma_kernel<D, NEG>), dim3(a.nsplit, groups, a.B), dim3(kThreads), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k_pool, (const uint16_t*)a.v_pool,
+                       a.page_table, a.seq_lens, a.ws, a.Hq, a.Hkv, ps_log2, a.nsplit, c2, a.window);
+}
+
+template <int D, bool NEG>
 void launch_split_d(const DecodeArgs& a, int GH, int ps_log2, float c2, hipStream_t stream) {
     switch (GH) {
         case 8: launch_split<D, 8, NEG>(a, ps_log2, c2, stream); break;
@@ -427,10 +772,19 @@ void launch_split_d(const DecodeArgs& a, int GH, int ps_log2, float c2, hipStrea
 
 }  // namespace
 
+// groups of eight and more query heads per K/V head take the MFMA kernel:
+// there the vector kernel is bound by its dot products (3.75 TB/s at 8 heads
+// against 4.3 for the MFMA kernel), while with four heads it streams at up to
+// 6 TB/s, more than the MFMA kernel's one workgroup per CU sustains
+bool decode_on_mfma(int G) { return G >= 8; }
+
 int decode_nsplit(int B, int Hq, int Hkv, int num_cu) {
     const int G = Hq / Hkv;
-    const long long units = (long long)B * Hkv * (G / heads_per_group(G));
-    const long long target = 8LL * (num_cu > 0 ? num_cu : 256);
+    const long long units = decode_on_mfma(G) ? (long long)B * Hkv * ((G + 31) / 32)
+                                               : (long long)B * Hkv * (G / heads_per_group(G));
+    // the MFMA kernel runs one workgroup per CU: fewer, longer splits amortise
+    // its start (sequence rank, q, the first two tiles in flight)
+    const long long target = (decode_on_mfma(G) ? 2LL : 8LL) * (num_cu > 0 ? num_cu : 256);
     long long n = (target + units - 1) / units;
     if (n < 1) n = 1;
     if (n > 64) n = 64;
@@ -447,7 +801,15 @@ hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream) {
     const float c2 = a.scale * 1.4426950408889634f;
     const int GH = heads_per_group(a.Hq / a.Hkv);
     const bool neg = a.scale < 0.f;
-    if (a.D == 128) {
+    if (decode_on_mfma(a.Hq / a.Hkv)) {
+        if (a.D == 128) {
+            if (neg) launch_mfma<128, true>(a, ps_log2, c2, stream);
+            else launch_mfma<128, false>(a, ps_log2, c2, stream);
+        } else {
+            if (neg) launch_mfma<64, true>(a, ps_log2, c2, stream);
+            else launch_mfma<64, false>(a, ps_log2, c2, stream);
+        }
+    } else if (a.D == 128) {
         if (neg) launch_split_d<128, true>(a, GH, ps_log2, c2, stream);
         else launch_split_d<128, false>(a, GH, ps_log2, c2, stream);
     } else {

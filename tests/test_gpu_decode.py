@@ -64,6 +64,12 @@ CASES = [
     (2, 8, 2, 128, 256, [300, 1000]),
     (2, 6, 2, 64, 128, [129, 2]),           # 3 heads per K/V head
     (64, 4, 2, 128, 16, list(range(1, 65))),
+    # eight and more heads per K/V head: the MFMA kernel
+    (4, 16, 2, 128, 16, [1, 31, 33, 2000]),
+    (3, 32, 2, 64, 8, [700, 65, 5]),
+    (2, 48, 1, 128, 32, [900, 40]),         # a group of 32 heads and one of 16
+    (2, 64, 1, 64, 256, [1500, 3]),         # MQA, two groups of 32
+    (40, 64, 8, 128, 16, [37 * i % 1900 + 1 for i in range(40)]),
 ]
 
 
@@ -166,6 +172,10 @@ def test_unusual_scales(scale):
     d = inputs.decode_inputs(5, 8, 2, 128, 16, 1, 700, "bf16", seed=37)
     check_bf16(f64(_run(d, scale)), _oracle(d, scale), f"scale {scale}")
     check_bf16(f64(_run_w(d, scale, 100)), _oracle_w(d, scale, 100), f"window 100, scale {scale}")
+    # eight heads per K/V head (the MFMA kernel)
+    d = inputs.decode_inputs(5, 16, 2, 128, 16, 1, 700, "bf16", seed=38)
+    check_bf16(f64(_run(d, scale)), _oracle(d, scale), f"8 heads per K/V head, scale {scale}")
+    check_bf16(f64(_run_w(d, scale, 100)), _oracle_w(d, scale, 100), f"8 heads, window 100, scale {scale}")
 
 
 # ---- sliding-window decode ------------------------------------------------------
@@ -191,6 +201,9 @@ WINDOW_CASES = [
     (2, 8, 2, 128, 256, [300, 1000], 333),
     (6, 8, 2, 128, 16, [3000, 2048, 4097, 17, 5000, 100], 2048),
     (64, 4, 2, 128, 16, list(range(1, 65)), 7),
+    (4, 16, 2, 128, 16, [1, 31, 33, 2000], 40),
+    (3, 32, 2, 64, 8, [700, 65, 5], 64),
+    (2, 48, 1, 128, 32, [900, 40], 500),
 ]
 
 
