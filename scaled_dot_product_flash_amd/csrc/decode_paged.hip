@@ -11,7 +11,11 @@
 // per-sequence page table and a global page pool).
 //
 // The step is bound by HBM bandwidth (every cached K/V byte is read once), so
-// the design is about bytes in flight and cheap per-byte VALU work, not MFMA:
+// the design is about bytes in flight and cheap per-byte VALU work. Up to 4
+// query heads per K/V head take the vector kernel below; 8 and more, whose
+// per-byte dot products would bound the vector kernel, take the MFMA kernel
+// further down (described there). Both write the same split partials.
+// The vector kernel:
 //  * Split kernel, grid (split, kv-head group, sequence). The query heads that
 //    share a K/V head (up to 8) are packed into one workgroup so each page is
 //    read once for all of them. The sequence's context is cut into `nsplit`
@@ -405,9 +409,9 @@ void decode_merge_kernel(const float* __restrict__ ws, uint16_t* __restrict__ Op
 // The query heads that share a K/V head form a small dense contraction with
 // the cached tokens: S^T (tokens x heads) = K Q^T and O^T (dims x heads) +=
 // V^T P^T. With up to 32 heads as the 32 columns of v_mfma_f32_32x32x16_bf16
-// the vector ALU is left with the softmax only, which keeps the step bound by
-// HBM for groups of 4 and more heads, where the vector kernel above spends
-// most of its time in dot products and lane sums.
+// the vector ALU is left with the softmax only. The launcher takes this kernel
+// for 8 and more heads per K/V head, where the vector kernel above is bound by
+// its dot products and lane sums.
 //  * Grid (split, kv head x head group of <= 32, sequence by length rank);
 //    a split's 32-token tiles are dealt round-robin to the four waves, each
 //    with its own online softmax; the waves merge at the end and the split's
