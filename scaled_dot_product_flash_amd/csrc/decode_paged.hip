@@ -11,7 +11,7 @@
 // per-sequence page table and a global page pool).
 //
 // The step is bound by HBM bandwidth (every cached K/V byte is read once), so
-// the design is about bytes in flight and cheap per-byte VALU work. Up to 4
+// the design is about bytes in flight and cheap per-byte VALU work. Fewer than 8
 // query heads per K/V head take the vector kernel below; 8 and more, whose
 // per-byte dot products would bound the vector kernel, take the MFMA kernel
 // further down (described there). Both write the same split partials.
