@@ -127,12 +127,13 @@ int decode_call(const void* q, const void* k_pool, const void* v_pool, const int
     int ncu = 0;
     int rc = cu_count(device, &ncu);
     if (rc != ATTN_OK) return rc;
-    const int nsplit = attn::decode_nsplit(B, Hq, Hkv, ncu);
+    const bool mfma = attn::decode_on_mfma(B, Hq, Hkv, D, ncu);
+    const int nsplit = attn::decode_nsplit(B, Hq, Hkv, ncu, mfma);
     float* ws = nullptr;
     rc = get_workspace(device, stream, attn::decode_workspace_floats(B, Hq, D, nsplit), &ws);
     if (rc != ATTN_OK) return rc;
     attn::DecodeArgs a{q, k_pool, v_pool, page_table, seq_lens, o, B, Hq, Hkv, D, page_size, scale, window,
-                       nsplit, ws};
+                       nsplit, ws, mfma};
     return hip_status(attn::launch_decode_paged(a, stream));
 }
 

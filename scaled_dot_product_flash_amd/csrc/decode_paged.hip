@@ -776,19 +776,28 @@ void launch_split_d(const DecodeArgs& a, int GH, int ps_log2, float c2, hipStrea
 
 }  // namespace
 
-// groups of eight and more query heads per K/V head take the MFMA kernel:
-// there the vector kernel is bound by its dot products (3.75 TB/s at 8 heads
-// against 4.3 for the MFMA kernel), while with four heads it streams at up to
-// 6 TB/s, more than the MFMA kernel's one workgroup per CU sustains
-bool decode_on_mfma(int G) { return G >= 8; }
-
-int decode_nsplit(int B, int Hq, int Hkv, int num_cu) {
+// Which decode kernel: the vector kernel runs three workgroups per CU and is
+// bound by its per-byte dot products as the heads per K/V head grow; the MFMA
+// kernel has no such cost but runs one workgroup per CU, so it needs the
+// splits of few (sequence, K/V head) units to fill the chip. Measured on
+// MI355X: 16 heads per K/V head, MFMA 1.8x; D = 64 with 8 heads, MFMA up to
+// 1.5x (at 512 units 5 % behind); D = 128 with 8 heads, MFMA 6-15 % ahead at
+// up to 128 units and the vector kernel 5-13 % ahead from 256 units; 4 heads,
+// the vector kernel (6 TB/s) well ahead.
+bool decode_on_mfma(int B, int Hq, int Hkv, int D, int num_cu) {
     const int G = Hq / Hkv;
-    const long long units = decode_on_mfma(G) ? (long long)B * Hkv * ((G + 31) / 32)
-                                               : (long long)B * Hkv * (G / heads_per_group(G));
+    if (G >= 16) return true;
+    if (G < 8) return false;
+    return D == 64 || (long long)B * Hkv * 2 <= (num_cu > 0 ? num_cu : 256);
+}
+
+int decode_nsplit(int B, int Hq, int Hkv, int num_cu, bool mfma) {
+    const int G = Hq / Hkv;
+    const long long units = mfma ? (long long)B * Hkv * ((G + 31) / 32)
+                                 : (long long)B * Hkv * (G / heads_per_group(G));
     // the MFMA kernel runs one workgroup per CU: fewer, longer splits amortise
     // its start (sequence rank, q, the first two tiles in flight)
-    const long long target = (decode_on_mfma(G) ? 2LL : 8LL) * (num_cu > 0 ? num_cu : 256);
+    const long long target = (mfma ? 2LL : 8LL) * (num_cu > 0 ? num_cu : 256);
     long long n = (target + units - 1) / units;
     if (n < 1) n = 1;
     if (n > 64) n = 64;
@@ -805,7 +814,7 @@ hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream) {
     const float c2 = a.scale * 1.4426950408889634f;
     const int GH = heads_per_group(a.Hq / a.Hkv);
     const bool neg = a.scale < 0.f;
-    if (decode_on_mfma(a.Hq / a.Hkv)) {
+    if (a.mfma) {
         if (a.D == 128) {
             if (neg) launch_mfma<128, true>(a, ps_log2, c2, stream);
             else launch_mfma<128, false>(a, ps_log2, c2, stream);

@@ -36,6 +36,7 @@ struct DecodeArgs {
     int window;     // 0: every cached token; W > 0: the W most recent
     int nsplit;     // context splits per (sequence, head group)
     float* ws;      // partial results, decode_workspace_floats() floats
+    bool mfma;      // decode_on_mfma(): the MFMA kernel instead of the vector one
 };
 
 struct AppendArgs {
@@ -69,7 +70,8 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 
 // Number of context splits for a decode call on a device with `num_cu`
 // compute units, and the workspace (in floats) those splits need.
-int decode_nsplit(int B, int Hq, int Hkv, int num_cu);
+bool decode_on_mfma(int B, int Hq, int Hkv, int D, int num_cu);
+int decode_nsplit(int B, int Hq, int Hkv, int num_cu, bool mfma);
 size_t decode_workspace_floats(int B, int Hq, int D, int nsplit);
 hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
