@@ -35,7 +35,9 @@
 //    query heads sharing a K/V head meet in the same L2. Contiguous K/V uses
 //    one chunk per XCD; a paged cache, whose sequences differ in length and
 //    are listed longest first, uses one (batch, kv head) group per chunk, so
-//    every XCD gets a like share of long and short sequences.
+//    every XCD gets a like share of long and short sequences. With fewer
+//    groups than XCDs (MQA, one sequence) a chunk is one query tile's heads,
+//    so every XCD gets a like share of heavy and light causal tiles.
 
 #include "launch.h"
 
@@ -73,12 +75,19 @@ __device__ __forceinline__ int dealt_item(int w, int chunk, int nitems) {
 }
 
 // Host side of the deal: the chunk size and the grid that covers every chunk.
+// With at least one (batch, kv head) group per XCD, contiguous K/V takes one
+// run of 1/8 of the list per XCD and a paged cache one group per chunk. With
+// fewer groups (MQA, a single sequence), a chunk is the G query heads of one
+// (group, query tile): with one run per XCD the heaviest query tiles would
+// all land on the first XCDs.
 struct Deal {
     long long chunk, grid;
 };
-inline Deal make_deal(long long nitems, long long group_items, bool paged) {
+inline Deal make_deal(long long nitems, long long group_items, int G, bool paged) {
     const long long per_xcd = (nitems + kXcds - 1) / kXcds;
-    const long long chunk = paged ? std::max(1LL, std::min(group_items, per_xcd)) : std::max(1LL, per_xcd);
+    const long long ngroups = (nitems + group_items - 1) / group_items;
+    long long chunk = ngroups < kXcds ? (long long)G : paged ? std::min(group_items, per_xcd) : per_xcd;
+    chunk = std::max(1LL, chunk);
     const long long nchunks = (nitems + chunk - 1) / chunk;
     const long long rounds = (nchunks + kXcds - 1) / kXcds;
     return {chunk, rounds * kXcds * chunk};
@@ -921,7 +930,7 @@ template <int NW, bool NEG, bool PAGED>
 hipError_t launch_pipe(const PrefillArgs& a, hipStream_t stream) {
     const int nqt = (a.Sq + 32 * NW - 1) / (32 * NW);
     const long long nitems = (long long)a.B * a.Hq * nqt;
-    const Deal deal = make_deal(nitems, (long long)(a.Hq / a.Hkv) * nqt, PAGED);
+    const Deal deal = make_deal(nitems, (long long)(a.Hq / a.Hkv) * nqt, a.Hq / a.Hkv, PAGED);
     if (deal.grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     float c2 = a.scale * 1.4426950408889634f;
     if (c2 == 0.f) c2 = 1e-30f;
@@ -938,7 +947,7 @@ template <int D, bool NEG, bool PAGED>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     const int nqt = (a.Sq + kBM - 1) / kBM;
     const long long nitems = (long long)a.B * a.Hq * nqt;
-    const Deal deal = make_deal(nitems, (long long)(a.Hq / a.Hkv) * nqt, PAGED);
+    const Deal deal = make_deal(nitems, (long long)(a.Hq / a.Hkv) * nqt, a.Hq / a.Hkv, PAGED);
     if (deal.grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     float c2 = a.scale * 1.4426950408889634f;
     // scale 0: a tiny positive factor gives bit-identical weights (all
