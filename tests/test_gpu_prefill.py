@@ -106,6 +106,11 @@ SHAPES = [
     (1, 2, 2, 60, 170, 64, True, 8),        # the same across a 128-key tile
     (2, 16, 4, 1000, 1000, 128, True, 0),
     (1, 4, 4, 1000, 1000, 64, True, 0),
+    # fewer (batch, kv head) groups than XCDs: one query tile's heads per
+    # chunk, dealt in snake order (the last rounds partly empty)
+    (1, 8, 1, 2000, 2000, 128, True, 0),
+    (1, 4, 2, 1300, 1300, 128, True, 0),
+    (2, 8, 1, 1500, 1500, 64, True, 0),
     # D = 64 over long key ranges (many 64-key tiles per row block)
     (1, 2, 1, 300, 4400, 64, True, 0),
     (1, 2, 2, 4200, 4200, 64, True, 1000),
