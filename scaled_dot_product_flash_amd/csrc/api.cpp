@@ -103,6 +103,10 @@ int prefill_call(bool f32, const void* q, const void* k, const void* v, void* o,
     if (want_lse && !lse) return ATTN_ERR_NULL;
     if (want_lse && !aligned4(lse)) return ATTN_ERR_ALIGN;
     attn::PrefillArgs a{q, k, v, o, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, want_lse ? lse : nullptr};
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return ATTN_ERR_HIP;
+    const int crc = cu_count(device, &a.num_cu);
+    if (crc != ATTN_OK) return crc;
     return hip_status(f32 ? attn::launch_prefill_f32(a, stream) : attn::launch_prefill_bf16(a, stream));
 }
 
@@ -181,6 +185,10 @@ int attn_fwd_paged(const void* q, const void* k_pool, const void* v_pool, const 
         return ATTN_ERR_ALIGN;
     attn::PrefillArgs a{q, k_pool, v_pool, o, B, Hq, Hkv, Sq, 0, D, scale, causal, window, lse,
                         page_table, seq_lens, page_size};
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return ATTN_ERR_HIP;
+    const int crc = cu_count(device, &a.num_cu);
+    if (crc != ATTN_OK) return crc;
     return hip_status(attn::launch_prefill_bf16(a, stream));
 }
 

@@ -22,6 +22,7 @@ struct PrefillArgs {
     const int32_t* page_table = nullptr;
     const int32_t* seq_lens = nullptr;
     int page_size = 0;
+    int num_cu = 0;  // compute units of the device (0: 256)
 };
 
 struct DecodeArgs {

@@ -66,8 +66,18 @@ constexpr int kXcds = 8;
 // Work item of workgroup w under the chunked snake deal (-1: no item). Slot s
 // of XCD x = w % 8 is position s % chunk of that XCD's (s / chunk)-th chunk;
 // its k-th chunk is the list's chunk 8k + x for even k and 8k + 7 - x for odd k.
-__device__ __forceinline__ int dealt_item(int w, int chunk, int nitems) {
-    const int x = w % kXcds, s = w / kXcds;
+// `pair` (one chunk per XCD, every item resident in one round, two workgroups
+// per CU or one): the second half of the XCD's list is taken in reverse, so
+// the workgroups that fill a CU's slots in the second pass over the CUs get
+// the light items and each CU a like share of heavy and light causal tiles.
+__device__ __forceinline__ int dealt_item(int w, int chunk, int nitems, int pair) {
+    const int x = w % kXcds;
+    int s = w / kXcds;
+    if (pair) {
+        const int n = min(chunk, nitems - x * chunk);
+        const int H = (n + 1) / 2;
+        if (s >= H && s < n) s = H + (n - 1 - s);
+    }
     const int k = s / chunk;
     const int c = kXcds * k + ((k & 1) ? kXcds - 1 - x : x);
     const long long item = (long long)c * chunk + s % chunk;
@@ -112,7 +122,7 @@ __global__ __launch_bounds__(kThreads, 2)
 void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
                          int Hq, int Hkv, int Sq, int Sk, float c2, int causal, int window,
-                         int nqt, int nitems, int chunk,
+                         int nqt, int nitems, int chunk, int pair,
                          const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int ps_log2) {
     constexpr int BN = 64;                // keys per tile
     constexpr int KB = BN / 32;           // 32-key blocks per tile
@@ -132,7 +142,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
 
     // ---- work item -------------------------------------------------------
     const int w = blockIdx.x;
-    const int item = dealt_item(w, chunk, nitems);
+    const int item = dealt_item(w, chunk, nitems, pair);
     if (item < 0) return;
     const int G = Hq / Hkv;
     const int hg = item % G;
@@ -474,7 +484,7 @@ __global__ __launch_bounds__(64 * NW, 2)
 void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
                          int Hq, int Hkv, int Sq, int Sk, float c2, int causal, int window,
-                         int nqt, int nitems, int chunk,
+                         int nqt, int nitems, int chunk, int pair,
                          const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int ps_log2) {
     constexpr int D = 128, BN = 64, KB = 2, KS = 4, DS = 8, DB = 4, CPR = 16;
     constexpr int TILE_BYTES = BN * D * 2;
@@ -488,7 +498,7 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     __shared__ __attribute__((aligned(16))) unsigned char v_lds1[TILE_BYTES];
 
     const int w = blockIdx.x;
-    const int item = dealt_item(w, chunk, nitems);
+    const int item = dealt_item(w, chunk, nitems, pair);
     if (item < 0) return;
     const int G = Hq / Hkv;
     const int hg = item % G;
@@ -936,9 +946,12 @@ hipError_t launch_pipe(const PrefillArgs& a, hipStream_t stream) {
     if (c2 == 0.f) c2 = 1e-30f;
     int ps_log2 = 0;
     while ((1 << ps_log2) < a.page_size) ++ps_log2;
+    // single round of causal items with one run per XCD: pair heavy and light
+    const long long slots = (long long)(a.num_cu > 0 ? a.num_cu : 256) * (NW == 4 ? 2 : 1);
+    const int pair = (!PAGED && a.causal && (long long)a.B * a.Hkv >= kXcds && deal.grid <= slots) ? 1 : 0;
     hipLaunchKernelGGL((prefill_pipe_kernel<NW, NEG, PAGED>), dim3((unsigned)deal.grid), dim3(64 * NW), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                       a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)deal.chunk,
+                       a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)deal.chunk, pair,
                        a.page_table, a.seq_lens, ps_log2);
     return hipGetLastError();
 }
@@ -957,7 +970,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     while ((1 << ps_log2) < a.page_size) ++ps_log2;
     hipLaunchKernelGGL((prefill_bf16_kernel<D, NEG, PAGED>), dim3((unsigned)deal.grid), dim3(kThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                       a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)deal.chunk,
+                       a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)deal.chunk, 0,
                        a.page_table, a.seq_lens, ps_log2);
     return hipGetLastError();
 }
