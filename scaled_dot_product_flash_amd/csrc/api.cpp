@@ -246,15 +246,17 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned4(lse) ||
         !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
         return ATTN_ERR_ALIGN;
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return ATTN_ERR_HIP;
     float* ws = nullptr;
     if (Sq > 0) {
-        int device = 0;
-        if (hipGetDevice(&device) != hipSuccess) return ATTN_ERR_HIP;
         const size_t floats = (attn::backward_workspace_bytes(B, Hq, Sq, D) + 3) / 4;
         const int rc = get_workspace(device, stream, floats, &ws);
         if (rc != ATTN_OK) return rc;
     }
     attn::BackwardArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, ws};
+    const int crc = cu_count(device, &a.num_cu);
+    if (crc != ATTN_OK) return crc;
     return hip_status(attn::launch_backward(a, stream));
 }
 

@@ -38,6 +38,7 @@
 // evaluate the mask.
 
 #include "launch.h"
+#include "deal.h"
 
 #include <cmath>
 #include <type_traits>
@@ -58,7 +59,6 @@ constexpr int kNW = 4;                 // waves per workgroup
 constexpr int kThreads = 64 * kNW;
 constexpr int kRows = 32 * kNW;        // query rows (dq) or keys (dkdv) per workgroup
 constexpr int kTile = 64;              // rows of a streamed K/V or Q/dO tile
-constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format).
 constexpr int kRsrcWord3 = 0x00020000;
@@ -164,7 +164,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                    float* __restrict__ Delta, float* __restrict__ L2, uint16_t* __restrict__ dQ,
                    uint16_t* __restrict__ QT,
                    uint16_t* __restrict__ dOT, int Hq, int Hkv, int Sq, int Sk, float scale, float c2, int causal,
-                   int window, int nqt, int nitems, int per_xcd, int nqb) {
+                   int window, int nqt, int nitems, int chunk, int pair, int nqb) {
     constexpr int BN = kTile, KB = BN / 32, DS = D / 16, DB = D / 32;
     constexpr int TILE_BYTES = BN * D * 2;
     __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILE_BYTES];
@@ -173,11 +173,11 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     __shared__ __attribute__((aligned(16))) unsigned char v_lds1[TILE_BYTES];
 
     // work item: (batch, kv head) major, then query tile from the heaviest
-    // causal one down, then the query heads of the group; each XCD takes a
-    // contiguous run of items
+    // causal one down, then the query heads of the group; dealt to the XCDs
+    // as the forward kernels deal theirs
     const int w = blockIdx.x;
-    const int item = (w % kXcds) * per_xcd + w / kXcds;
-    if (item >= nitems) return;
+    const int item = dealt_item(w, chunk, nitems, pair);
+    if (item < 0) return;
     const int G = Hq / Hkv;
     const int hg = item % G;
     const int r1 = item / G;
@@ -698,13 +698,17 @@ hipError_t launch_d(const BackwardArgs& a, hipStream_t stream) {
     if (a.Sq > 0) {
         const int nqt = (a.Sq + kRows - 1) / kRows;
         const long long nitems = (long long)a.B * a.Hq * nqt;
-        const long long per_xcd = (nitems + kXcds - 1) / kXcds;
-        const long long grid = per_xcd * kXcds;
+        const int G = a.Hq / a.Hkv;
+        const Deal deal = make_deal(nitems, (long long)G * nqt, G, false);
+        const long long grid = deal.grid;
+        // one round of causal items (two workgroups per CU): pair heavy and light
+        const long long slots = 2LL * (a.num_cu > 0 ? a.num_cu : 256);
+        const int pair = (a.causal && (long long)a.B * a.Hkv >= kXcds && grid <= slots) ? 1 : 0;
         if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
         hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o,
                            (const uint16_t*)a.dout, a.lse, delta, l2, (uint16_t*)a.dq, qt, dot, a.Hq, a.Hkv, a.Sq, a.Sk,
-                           a.scale, c2, a.causal, a.window, nqt, (int)nitems, (int)per_xcd, nqb);
+                           a.scale, c2, a.causal, a.window, nqt, (int)nitems, (int)deal.chunk, pair, nqb);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

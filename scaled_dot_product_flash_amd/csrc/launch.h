@@ -64,6 +64,7 @@ struct BackwardArgs {
     float scale;
     int causal, window;
     void* ws;           // workspace of backward_workspace_bytes(B, Hq, Sq, D) bytes
+    int num_cu = 0;     // compute units of the device (0: 256)
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
