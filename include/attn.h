@@ -276,8 +276,13 @@ int attn_pages_table(const attn_page_pool* pool, const int64_t* seq_ids, int n, 
  *   they must not overlap the inputs. Arithmetic: bf16 MFMA products with
  *   float32 accumulation; P and dS are rounded to bf16 as MFMA operands, and
  *   rowsum(dout * o) uses the bf16 o.
- *   Scratch: B * Hq * Sq floats of the per-(device, stream) workspace that
- *   attn_decode_paged also uses (grown on demand, freed by attn_release).
+ *   Scratch, in the per-(device, stream) workspace that attn_decode_paged
+ *   also uses (grown on demand, freed by attn_release): 2 * B * Hq * Sq
+ *   floats (rowsum(dout * o) and the lse in log2 units), transposed copies of
+ *   q and dout (2 * B * Hq * Sq * D bf16, Sq rounded up to 32), and, when the
+ *   (batch, kv head, 256-key) blocks are too few to fill the device, float32
+ *   partial dk and dv of up to 16 runs per block (2 * runs * B * Hkv * Sk * D
+ *   floats), summed in a fixed order: the result is bit-reproducible.
  *   Errors: those of attn_fwd for the same sizes, plus NULL / ALIGN for the
  *   extra pointers, NOMEM for the workspace, and SHAPE when Sq * D or Sk * D
  *   exceeds 2^29 (one head's rows are addressed with 32-bit offsets).

@@ -248,15 +248,19 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
         return ATTN_ERR_ALIGN;
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return ATTN_ERR_HIP;
+    int ncu = 0;
+    const int crc = cu_count(device, &ncu);
+    if (crc != ATTN_OK) return crc;
+    const int kv_splits = attn::backward_kv_splits(B, Hkv, Sq, Sk, ncu);
     float* ws = nullptr;
     if (Sq > 0) {
-        const size_t floats = (attn::backward_workspace_bytes(B, Hq, Sq, D) + 3) / 4;
+        const size_t floats = (attn::backward_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, kv_splits) + 3) / 4;
         const int rc = get_workspace(device, stream, floats, &ws);
         if (rc != ATTN_OK) return rc;
     }
     attn::BackwardArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, ws};
-    const int crc = cu_count(device, &a.num_cu);
-    if (crc != ATTN_OK) return crc;
+    a.num_cu = ncu;
+    a.kv_splits = kv_splits;
     return hip_status(attn::launch_backward(a, stream));
 }
 

@@ -428,6 +428,13 @@ __device__ __forceinline__ void dma_tblock(__amdgpu_buffer_rsrc_t rs, unsigned s
 // major: under a causal mask the first key blocks carry the most work and go
 // first, and with (batch, kv head) = blockIdx % (B * Hkv) one (batch, kv head)
 // stays on one XCD when B * Hkv is a multiple of 8.
+//
+// When the key blocks are too few to fill the chip (MQA, a single sequence),
+// each key block's steps are cut into `nsplit` contiguous runs, one workgroup
+// each (blockIdx = (key block * nsplit + split) * B * Hkv + (batch, kv head));
+// the runs write float32 partial dK (already scaled) and dV to `part`, which
+// bwd_kv_reduce_kernel sums in split order into the bf16 outputs. With one
+// run the kernel writes dK and dV itself.
 template <int D>
 __global__ __launch_bounds__(64 * kKvWaves, 1)
 void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -435,7 +442,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                      const uint16_t* __restrict__ QT, const uint16_t* __restrict__ dOT,
                      const float* __restrict__ L2, const float* __restrict__ Delta, uint16_t* __restrict__ dK,
                      uint16_t* __restrict__ dV, int Hq, int Hkv, int Sq, int Sk, float scale, float c2, int causal,
-                     int window, int nqb, int nbg) {
+                     int window, int nqb, int nbg, int nsplit, float* __restrict__ part) {
     constexpr int NW = kKvWaves, DS = D / 16, DB = D / 32, NP = 2 * DB;
     constexpr int RT = kQB * D * 2;   // bytes of a row tile and of a transposed block
     __shared__ __attribute__((aligned(16))) unsigned char v_lds[kKvKeys * D * 2];
@@ -453,7 +460,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     __shared__ __attribute__((aligned(16))) float d_lds1[64];
 
     const int w = blockIdx.x;
-    const int kt = w / nbg;
+    const int kt = w / (nbg * nsplit);
+    const int split = (w / nbg) % nsplit;
     const int bg = w % nbg;
     const int G = Hq / Hkv;
     const int g = bg % Hkv;
@@ -489,6 +497,9 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const int t_hi = q_hi / kQB;
     const int nt = q_lo <= q_hi ? t_hi - q_lo / kQB + 1 : 0;
     const int nsteps = G * nt;
+    // this workgroup's run of steps
+    const int s_begin = (int)((long long)nsteps * split / nsplit);
+    const int s_end = (int)((long long)nsteps * (split + 1) / nsplit);
 
     f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -638,7 +649,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     // every LDS address is a constant offset)
     auto step = [&](int s, auto r2) __attribute__((always_inline)) {
         constexpr int R = decltype(r2)::value;
-        if (s + 1 < nsteps)
+        if (s + 1 < s_end)
             issue(s + 1, R ? q_lds0 : q_lds1, R ? o_lds0 : o_lds1, R ? l_lds0 : l_lds1, R ? d_lds0 : d_lds1,
                   R ? qt_lds0 : qt_lds1, R ? ot_lds0 : ot_lds1);
         bool edge;
@@ -652,20 +663,36 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         __syncthreads();
     };
 
-    if (nsteps > 0) {
+    if (s_end > s_begin) {
         // the workgroup's V rows stay in LDS for the whole kernel
         dma_rows<D, kKvKeys, NW>(rsrc(V + kv_base, Sk * D * 2), k0, v_lds, wave, lane);
-        issue(0, q_lds0, o_lds0, l_lds0, d_lds0, qt_lds0, ot_lds0);
+        issue(s_begin, q_lds0, o_lds0, l_lds0, d_lds0, qt_lds0, ot_lds0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        for (int s = 0; s < nsteps; s += 2) {
+        for (int s = s_begin; s < s_end; s += 2) {
             step(s, std::integral_constant<int, 0>());
-            if (s + 1 < nsteps) step(s + 1, std::integral_constant<int, 1>());
+            if (s + 1 < s_end) step(s + 1, std::integral_constant<int, 1>());
         }
     }
 
     // accumulator value v of block db holds d = 32 db + 8(v/4) + 4hh + v%4
     if (!key_ok) return;
+    if (part != nullptr) {
+        const size_t plane = (size_t)nbg * Sk * D;
+        float* kp = part + (size_t)split * plane + ((size_t)bg * Sk + key) * D;
+        float* vp = part + (size_t)(nsplit + split) * plane + ((size_t)bg * Sk + key) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d = 32 * db + 8 * r + 4 * hh;
+                *reinterpret_cast<float4*>(kp + d) = make_float4(dk[db][4 * r] * scale, dk[db][4 * r + 1] * scale,
+                                                                 dk[db][4 * r + 2] * scale, dk[db][4 * r + 3] * scale);
+                *reinterpret_cast<float4*>(vp + d) =
+                    make_float4(dv[db][4 * r], dv[db][4 * r + 1], dv[db][4 * r + 2], dv[db][4 * r + 3]);
+            }
+        return;
+    }
     uint16_t* kout = dK + kv_base + (size_t)key * D;
     uint16_t* vout = dV + kv_base + (size_t)key * D;
 #pragma unroll
@@ -678,6 +705,24 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             *reinterpret_cast<uint2*>(vout + d) =
                 pack4(dv[db][4 * r], dv[db][4 * r + 1], dv[db][4 * r + 2], dv[db][4 * r + 3]);
         }
+}
+
+// dK, dV of a split key block: the sum, in split order, of the runs' float32
+// partials (four elements per thread), rounded to bf16
+__global__ __launch_bounds__(256)
+void bwd_kv_reduce_kernel(const float* __restrict__ part, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+                          long long plane, int nsplit) {
+    const long long i = 4 * ((long long)blockIdx.x * 256 + threadIdx.x);
+    if (i >= plane) return;
+    float4 k = make_float4(0.f, 0.f, 0.f, 0.f), v = k;
+    for (int z = 0; z < nsplit; ++z) {
+        const float4 a = *reinterpret_cast<const float4*>(part + (size_t)z * plane + i);
+        const float4 c = *reinterpret_cast<const float4*>(part + (size_t)(nsplit + z) * plane + i);
+        k.x += a.x; k.y += a.y; k.z += a.z; k.w += a.w;
+        v.x += c.x; v.y += c.y; v.z += c.z; v.w += c.w;
+    }
+    *reinterpret_cast<uint2*>(dK + i) = pack4(k.x, k.y, k.z, k.w);
+    *reinterpret_cast<uint2*>(dV + i) = pack4(v.x, v.y, v.z, v.w);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -714,20 +759,44 @@ hipError_t launch_d(const BackwardArgs& a, hipStream_t stream) {
     }
     const int nkt = (a.Sk + kKvKeys - 1) / kKvKeys;
     const int nbg = a.B * a.Hkv;
-    const long long grid = (long long)nbg * nkt;
+    const int nsplit = a.Sq > 0 ? a.kv_splits : 1;
+    float* part = nsplit > 1 ? reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(dot) + align256(tbytes))
+                             : nullptr;
+    const long long grid = (long long)nbg * nkt * nsplit;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)grid), dim3(64 * kKvWaves), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                        qt, dot, l2, delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.Hq, a.Hkv, a.Sq, a.Sk, a.scale, c2,
-                       a.causal, a.window, nqb, nbg);
+                       a.causal, a.window, nqb, nbg, nsplit, part);
+    if (nsplit > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const long long plane = (long long)nbg * a.Sk * D;
+        const long long blocks = (plane / 4 + 255) / 256;
+        hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const float*)part,
+                           (uint16_t*)a.dk, (uint16_t*)a.dv, plane, nsplit);
+    }
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t backward_workspace_bytes(int B, int Hq, int Sq, int D) {
+int backward_kv_splits(int B, int Hkv, int Sq, int Sk, int num_cu) {
+    // enough dK/dV workgroups for two per CU, at most 16 runs per key block
+    if (Sq <= 0) return 1;
+    const long long units = (long long)B * Hkv * ((Sk + kKvKeys - 1) / kKvKeys);
+    const long long target = 2LL * (num_cu > 0 ? num_cu : 256);
+    long long n = units > 0 ? (target + units - 1) / units : 1;
+    if (n < 1) n = 1;
+    if (n > 16) n = 16;
+    return (int)n;
+}
+
+size_t backward_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, int kv_splits) {
     const size_t nqb = (size_t)(Sq + kQB - 1) / kQB;
-    return 2 * align256((size_t)B * Hq * Sq * 4) + 2 * align256((size_t)B * Hq * nqb * kQB * D * 2);
+    size_t bytes = 2 * align256((size_t)B * Hq * Sq * 4) + 2 * align256((size_t)B * Hq * nqb * kQB * D * 2);
+    if (kv_splits > 1) bytes += 2 * (size_t)kv_splits * B * Hkv * Sk * D * 4;
+    return bytes;
 }
 
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {

@@ -63,8 +63,9 @@ struct BackwardArgs {
     int B, Hq, Hkv, Sq, Sk, D;
     float scale;
     int causal, window;
-    void* ws;           // workspace of backward_workspace_bytes(B, Hq, Sq, D) bytes
+    void* ws;           // workspace of backward_workspace_bytes(..., kv_splits) bytes
     int num_cu = 0;     // compute units of the device (0: 256)
+    int kv_splits = 1;  // backward_kv_splits(): runs per dK/dV key block
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
@@ -77,7 +78,8 @@ int decode_nsplit(int B, int Hq, int Hkv, int num_cu, bool mfma);
 size_t decode_workspace_floats(int B, int Hq, int D, int nsplit);
 hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
-size_t backward_workspace_bytes(int B, int Hq, int Sq, int D);
+int backward_kv_splits(int B, int Hkv, int Sq, int Sk, int num_cu);
+size_t backward_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, int kv_splits);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 
 }  // namespace attn

@@ -49,6 +49,7 @@ CASES = [
     (1, 8, 1, 200, 200, 128, True, 0),        # eight query heads on one K/V head
     (2, 4, 2, 65, 65, 128, True, 17),         # one tile plus one row, window
     (1, 2, 2, 600, 300, 128, False, 0),       # full attention, more queries than keys, MHA
+    (1, 8, 1, 1500, 1500, 64, True, 0),       # MQA: key blocks split into runs, partials summed
 ]
 
 
@@ -93,7 +94,8 @@ def test_backward_without_query_rows_zeroes_dk_dv():
 
 
 def test_backward_is_deterministic():
-    # dk, dv are plain stores and dq one workgroup's sum: repeated calls agree bit for bit
+    # dk, dv are plain stores or a fixed-order sum of split partials (this
+    # shape is split) and dq one workgroup's sum: repeated calls agree bit for bit
     say("backward determinism")
     q, k, v, do = cuda(*inputs.backward_inputs(1, 4, 2, 700, 700, 128, seed=5))
     o, lse = attn.fwd_lse(q, k, v, causal=True)
