@@ -940,9 +940,13 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     const bool neg = a.scale < 0.f;
     // D = 128: 256-row workgroups (eight waves) unless that leaves fewer than
-    // two workgroups per CU, then 128-row ones (four waves) for balance
+    // two workgroups per CU, or the keys are at most 2048, then 128-row ones
+    // (four waves, two per CU): a short item spends much of its time in the
+    // diagonal tiles (half as many with 128 rows) and in its start, which the
+    // second workgroup of the CU overlaps (16 x 32 heads x 1024 tokens causal:
+    // 524 -> 637 TFLOP/s; at 4096 keys the eight-wave kernel is ahead)
     const long long wg256 = (long long)a.B * a.Hq * ((a.Sq + 255) / 256);
-    const bool small = wg256 < 2LL * 256;
+    const bool small = wg256 < 2LL * 256 || (a.page_table == nullptr && a.Sk <= 2048);
     if (a.page_table != nullptr) {  // paged K/V
         if (a.D == 64) return neg ? launch_t<64, true, true>(a, stream) : launch_t<64, false, true>(a, stream);
         if (small) return neg ? launch_pipe<4, true, true>(a, stream) : launch_pipe<4, false, true>(a, stream);
