@@ -176,7 +176,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     // causal one down, then the query heads of the group; dealt to the XCDs
     // as the forward kernels deal theirs
     const int w = blockIdx.x;
-    const int item = dealt_item(w, chunk, nitems, pair);
+    const int item = dealt_item(w, chunk, nitems, pair, nqt, Hq / Hkv);
     if (item < 0) return;
     const int G = Hq / Hkv;
     const int hg = item % G;
@@ -746,9 +746,8 @@ hipError_t launch_d(const BackwardArgs& a, hipStream_t stream) {
         const int G = a.Hq / a.Hkv;
         const Deal deal = make_deal(nitems, (long long)G * nqt, G, false);
         const long long grid = deal.grid;
-        // one round of causal items (two workgroups per CU): pair heavy and light
-        const long long slots = 2LL * (a.num_cu > 0 ? a.num_cu : 256);
-        const int pair = (a.causal && (long long)a.B * a.Hkv >= kXcds && grid <= slots) ? 1 : 0;
+        // one round of causal items (two workgroups per CU): balance the CUs
+        const int pair = balance_arg(nitems, deal.chunk, (long long)G * nqt, grid, a.causal, a.num_cu, 2);
         if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
         hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o,

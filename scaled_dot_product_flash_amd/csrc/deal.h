@@ -14,22 +14,43 @@ constexpr int kXcds = 8;   // XCDs of an MI355X; workgroup w is dispatched to XC
 // Work item of workgroup w under the chunked snake deal (-1: no item). Slot s
 // of XCD x = w % 8 is position s % chunk of that XCD's (s / chunk)-th chunk;
 // its k-th chunk is the list's chunk 8k + x for even k and 8k + 7 - x for odd k.
-// `pair` (one chunk per XCD, every item resident in one round, two workgroups
-// per CU or one): the second half of the XCD's list is taken in reverse, so
-// the workgroups that fill a CU's slots in the second pass over the CUs get
-// the light items and each CU a like share of heavy and light causal tiles.
-__device__ __forceinline__ int dealt_item(int w, int chunk, int nitems, int pair) {
+//
+// `bal` > 0 (one chunk per XCD holding whole groups, every item resident in
+// one round of dispatch, bal = CUs per XCD): the dispatcher hands the XCD's
+// slots s = 0, 1, ... to its CUs round by round, slot s to CU s % bal. The
+// XCD's items are then taken by weight rank, query tiles heaviest first (then
+// the groups, then the heads of a group), and the ranks run forward over the
+// CUs in even rounds and backward in odd ones, so each CU gets a like mix of
+// heavy and light causal tiles. A partial last round keeps slot order.
+__device__ __forceinline__ int dealt_item(int w, int chunk, int nitems, int bal, int nqt, int G) {
     const int x = w % kXcds;
-    int s = w / kXcds;
-    if (pair) {
-        const int n = min(chunk, nitems - x * chunk);
-        const int H = (n + 1) / 2;
-        if (s >= H && s < n) s = H + (n - 1 - s);
+    const int s = w / kXcds;
+    if (bal > 0) {
+        const int n = min(chunk, nitems - x * chunk);   // this XCD's items: whole groups
+        if (s >= n) return -1;
+        const int r = s / bal, p = s % bal;
+        const bool partial_last = r == (n - 1) / bal && n % bal != 0;
+        const int rank = ((r & 1) && !partial_last) ? r * bal + (bal - 1 - p) : s;
+        const int per_tile = n / nqt;                    // groups of this XCD x G
+        const int qi = rank / per_tile, rest = rank % per_tile;
+        return x * chunk + ((rest / G) * nqt + qi) * G + rest % G;
     }
     const int k = s / chunk;
     const int c = kXcds * k + ((k & 1) ? kXcds - 1 - x : x);
     const long long item = (long long)c * chunk + s % chunk;
     return item < nitems ? (int)item : -1;
+}
+
+// `bal` argument of dealt_item for a launch: CUs per XCD when the deal is one
+// chunk per XCD of whole groups and every item is resident at once (the grid
+// fits `slots_per_cu` workgroups on each CU), causal items only; else 0.
+inline int balance_arg(long long nitems, long long chunk, long long group_items, long long grid, int causal,
+                       int num_cu, int slots_per_cu) {
+    const int cus = num_cu > 0 ? num_cu : 256;
+    const bool one_chunk_per_xcd = (nitems + chunk - 1) / chunk <= kXcds;
+    const bool whole_groups = chunk % group_items == 0;
+    const bool one_round = grid <= (long long)cus * slots_per_cu;
+    return (causal && one_chunk_per_xcd && whole_groups && one_round && cus % kXcds == 0) ? cus / kXcds : 0;
 }
 
 // Host side of the deal: the chunk size and the grid that covers every chunk.

@@ -102,7 +102,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
 
     // ---- work item -------------------------------------------------------
     const int w = blockIdx.x;
-    const int item = dealt_item(w, chunk, nitems, pair);
+    const int item = dealt_item(w, chunk, nitems, pair, nqt, Hq / Hkv);
     if (item < 0) return;
     const int G = Hq / Hkv;
     const int hg = item % G;
@@ -458,7 +458,7 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     __shared__ __attribute__((aligned(16))) unsigned char v_lds1[TILE_BYTES];
 
     const int w = blockIdx.x;
-    const int item = dealt_item(w, chunk, nitems, pair);
+    const int item = dealt_item(w, chunk, nitems, pair, nqt, Hq / Hkv);
     if (item < 0) return;
     const int G = Hq / Hkv;
     const int hg = item % G;
@@ -906,9 +906,11 @@ hipError_t launch_pipe(const PrefillArgs& a, hipStream_t stream) {
     if (c2 == 0.f) c2 = 1e-30f;
     int ps_log2 = 0;
     while ((1 << ps_log2) < a.page_size) ++ps_log2;
-    // single round of causal items with one run per XCD: pair heavy and light
-    const long long slots = (long long)(a.num_cu > 0 ? a.num_cu : 256) * (NW == 4 ? 2 : 1);
-    const int pair = (!PAGED && a.causal && (long long)a.B * a.Hkv >= kXcds && deal.grid <= slots) ? 1 : 0;
+    // one round of causal items, one run of whole groups per XCD: balance the
+    // CUs by weight (four waves: two workgroups per CU, eight waves: one)
+    const int pair = PAGED ? 0
+                           : balance_arg(nitems, deal.chunk, (long long)(a.Hq / a.Hkv) * nqt, deal.grid, a.causal,
+                                         a.num_cu, NW == 4 ? 2 : 1);
     hipLaunchKernelGGL((prefill_pipe_kernel<NW, NEG, PAGED>), dim3((unsigned)deal.grid), dim3(64 * NW), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                        a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)deal.chunk, pair,
@@ -922,6 +924,10 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     const long long nitems = (long long)a.B * a.Hq * nqt;
     const Deal deal = make_deal(nitems, (long long)(a.Hq / a.Hkv) * nqt, a.Hq / a.Hkv, PAGED);
     if (deal.grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    // one round of causal items (three workgroups per CU): balance the CUs
+    const int pair = PAGED ? 0
+                           : balance_arg(nitems, deal.chunk, (long long)(a.Hq / a.Hkv) * nqt, deal.grid, a.causal,
+                                         a.num_cu, 3);
     float c2 = a.scale * 1.4426950408889634f;
     // scale 0: a tiny positive factor gives bit-identical weights (all
     // exp2(0) = 1 for finite logits) and keeps masked logits at -inf
@@ -930,7 +936,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     while ((1 << ps_log2) < a.page_size) ++ps_log2;
     hipLaunchKernelGGL((prefill_bf16_kernel<D, NEG, PAGED>), dim3((unsigned)deal.grid), dim3(kThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                       a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)deal.chunk, 0,
+                       a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)deal.chunk, pair,
                        a.page_table, a.seq_lens, ps_log2);
     return hipGetLastError();
 }
