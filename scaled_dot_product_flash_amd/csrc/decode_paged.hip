@@ -417,10 +417,13 @@ void decode_merge_kernel(const float* __restrict__ ws, uint16_t* __restrict__ Op
 //    with its own online softmax; the waves merge at the end and the split's
 //    partial (m, l, o) goes to the same workspace as the vector kernel's.
 //  * K tiles go from HBM straight into registers in the MFMA operand layout
-//    (lane%32 = token, 8-dim chunks), two tiles ahead of use; V tiles go by
-//    buffer->LDS DMA into three LDS stages per wave and are read back with
-//    the transposing LDS read as the V^T operand. Page ids are scalar loads,
-//    so waiting for them never waits for the K/V loads in flight.
+//    (lane%32 = token, 8-dim chunks), one tile ahead of use; V tiles go by
+//    buffer->LDS DMA into two LDS stages per wave and are read back with the
+//    transposing LDS read as the V^T operand. Page ids are scalar loads, so
+//    waiting for them never waits for the K/V loads in flight. With two
+//    stages the kernel fits two workgroups per CU at D = 128 (207 VGPRs,
+//    66 KB of LDS) and four at D = 64: more independent waves hide the load
+//    latency better than deeper stages in one workgroup per CU did.
 //  * Every step issues the same instructions: tokens past the length are
 //    clamped to the last token for the K loads (valid memory, masked logits)
 //    and read as zeros for V (range check), and past a wave's last tile the
@@ -436,12 +439,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer resource word 3, gfx9 family
 constexpr int kTT = 32;                  // tokens per tile
-constexpr int kStages = 3;               // tiles per wave: one in use, two in flight
+constexpr int kStages = 2;               // tiles per wave: one in use, one in flight (V stages below)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
 
 template <int D, bool NEG>
-__global__ __launch_bounds__(kThreads, 1)
+__global__ __launch_bounds__(kThreads, 2)
 void decode_mfma_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __restrict__ Kp,
                         const uint16_t* __restrict__ Vp, const int32_t* __restrict__ table,
                         const int32_t* __restrict__ lens, float* __restrict__ ws,
@@ -458,7 +461,6 @@ void decode_mfma_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __restr
     // compiler's wait for DMA into LDS can tell the stages apart
     __shared__ __attribute__((aligned(16))) unsigned char vl0[kWaves * VT];
     __shared__ __attribute__((aligned(16))) unsigned char vl1[kWaves * VT];
-    __shared__ __attribute__((aligned(16))) unsigned char vl2[kWaves * VT];
     __shared__ float sh_m[kWaves * 32];
     __shared__ float sh_l[kWaves * 32];
     __shared__ int sh_len[kThreads];
@@ -552,7 +554,6 @@ void decode_mfma_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __restr
     auto vswz = [](int row) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); };
     unsigned char* const vs0 = vl0 + wave * VT;       // this wave's V stages
     unsigned char* const vs1 = vl1 + wave * VT;
-    unsigned char* const vs2 = vl2 + wave * VT;
 
     // issue tile t (this wave's k-th) into stage st: K into kdst registers,
     // V into LDS. The tile's pages are up to four consecutive table entries,
@@ -672,23 +673,20 @@ void decode_mfma_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __restr
 
     // three register sets for K, rotated with the V stages; tile k of this
     // wave is tile tbeg + wave + 4 k
-    uint4 k0[DS], k1[DS], k2[DS];
+    uint4 k0[DS], k1[DS];
     issue(tbeg + wave, vs0, k0, nmine <= 0);
-    issue(tbeg + wave + kWaves, vs1, k1, nmine <= 1);
     int k = 0;
     auto stage_step = [&](uint4 (&kc)[DS], uint4 (&kn)[DS], const unsigned char* vc, unsigned char* vn)
         __attribute__((always_inline)) {
-        // issue tile k + 2 into the stage tile k - 1 used, then tile k
-        issue(tbeg + wave + kWaves * (k + 2), vn, kn, k + 2 >= nmine);
+        // issue tile k + 1 into the stage tile k - 1 used, then tile k
+        issue(tbeg + wave + kWaves * (k + 1), vn, kn, k + 1 >= nmine);
         compute(tbeg + wave + kWaves * k, kc, vc);
         ++k;
     };
     while (k < nmine) {
-        stage_step(k0, k2, vs0, vs2);
+        stage_step(k0, k1, vs0, vs1);
         if (k >= nmine) break;
         stage_step(k1, k0, vs1, vs0);
-        if (k >= nmine) break;
-        stage_step(k2, k1, vs2, vs1);
     }
 
     // merge the waves: per head column, (m, l) and O^T rows through LDS
@@ -776,28 +774,27 @@ void launch_split_d(const DecodeArgs& a, int GH, int ps_log2, float c2, hipStrea
 
 }  // namespace
 
-// Which decode kernel: the vector kernel runs three workgroups per CU and is
-// bound by its per-byte dot products as the heads per K/V head grow; the MFMA
-// kernel has no such cost but runs one workgroup per CU, so it needs the
-// splits of few (sequence, K/V head) units to fill the chip. Measured on
-// MI355X: 16 heads per K/V head, MFMA 1.8x; D = 64 with 8 heads, MFMA up to
-// 1.5x (at 512 units 5 % behind); D = 128 with 8 heads, MFMA 6-15 % ahead at
-// up to 128 units and the vector kernel 5-13 % ahead from 256 units; 4 heads,
-// the vector kernel (6 TB/s) well ahead.
+// Which decode kernel: the vector kernel (three workgroups per CU) is bound
+// by its per-byte dot products as the heads per K/V head grow; the MFMA
+// kernel (two per CU at D = 128, four at D = 64) has no such cost. Measured
+// on MI355X over ten shapes with 8 and more heads per K/V head, the MFMA
+// kernel is 6-23 % ahead at D = 128 below 512 (sequence, K/V head) units,
+// level at 384 and 3 % behind at 512, up to 1.7x ahead at D = 64 and 1.95x
+// at 16 heads; with 4 heads the vector kernel (6 TB/s) is well ahead.
 bool decode_on_mfma(int B, int Hq, int Hkv, int D, int num_cu) {
     const int G = Hq / Hkv;
     if (G >= 16) return true;
     if (G < 8) return false;
-    return D == 64 || (long long)B * Hkv * 2 <= (num_cu > 0 ? num_cu : 256);
+    return D == 64 || (long long)B * Hkv < 2LL * (num_cu > 0 ? num_cu : 256);
 }
 
 int decode_nsplit(int B, int Hq, int Hkv, int num_cu, bool mfma) {
     const int G = Hq / Hkv;
     const long long units = mfma ? (long long)B * Hkv * ((G + 31) / 32)
                                  : (long long)B * Hkv * (G / heads_per_group(G));
-    // the MFMA kernel runs one workgroup per CU: fewer, longer splits amortise
-    // its start (sequence rank, q, the first two tiles in flight)
-    const long long target = (mfma ? 2LL : 8LL) * (num_cu > 0 ? num_cu : 256);
+    // the MFMA kernel holds fewer workgroups per CU: fewer, longer splits
+    // amortise its start (sequence rank, q, the first tile in flight)
+    const long long target = (mfma ? 4LL : 8LL) * (num_cu > 0 ? num_cu : 256);
     long long n = (target + units - 1) / units;
     if (n < 1) n = 1;
     if (n > 64) n = 64;
