@@ -566,6 +566,12 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             P[v] = 0.f;
         }
         bf16x8 aqo = ld16(qb + aq), aoo = ld16(ob + aq), avo = ld16(v_lds + av);
+        // the two waves of a SIMD meet at every barrier and would run their
+        // MFMA and softmax phases side by side; a raised priority while a wave
+        // issues MFMAs lets the first one through its block, so the other's
+        // VALU work overlaps it (about 1.5 % on the dK/dV kernel; in the dQ
+        // kernel, two workgroups per CU and no such lockstep, it costs 2 %)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < DS; ++st) {
             bf16x8 nq = aqo, no = aoo, nv = avo;
@@ -582,6 +588,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             aoo = no;
             avo = nv;
         }
+        __builtin_amdgcn_s_setprio(0);
         // accumulator value v holds query row 8(v/4) + 4hh + v%4 of the step;
         // masked pairs get an exponent of -inf, so P = 0 and dS = 0 exactly
 #pragma unroll
@@ -628,6 +635,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         int at = ln * 64 + ((((ln >> 2) & 3) ^ hh) << 4);
         asm volatile("" : "+v"(at));
         bf16x8 to = ld16(otb + at), tq = ld16(qtb + at);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int x = 0; x < NP; ++x) {
             const int c = x / DB, d = x % DB;
@@ -643,6 +651,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             to = no;
             tq = nq;
         }
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // step s, its tiles in the buffers of parity R (compile-time, so that
