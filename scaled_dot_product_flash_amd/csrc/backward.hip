@@ -755,7 +755,7 @@ hipError_t launch_d(const BackwardArgs& a, hipStream_t stream) {
         const int G = a.Hq / a.Hkv;
         const Deal deal = make_deal(nitems, (long long)G * nqt, G, false);
         const long long grid = deal.grid;
-        // one round of causal items (two workgroups per CU): balance the CUs
+        // causal items: order by weight (two workgroups per CU)
         const int pair = balance_arg(nitems, deal.chunk, (long long)G * nqt, grid, a.causal, a.num_cu, 2);
         if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
         hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,

@@ -37,7 +37,10 @@
 //    are listed longest first, uses one (batch, kv head) group per chunk, so
 //    every XCD gets a like share of long and short sequences. With fewer
 //    groups than XCDs (MQA, one sequence) a chunk is one query tile's heads,
-//    so every XCD gets a like share of heavy and light causal tiles.
+//    so every XCD gets a like share of heavy and light causal tiles. With
+//    causal contiguous K/V and a single round of workgroups, or groups too
+//    small to fill two rounds of an XCD, each XCD takes its items heaviest
+//    query tile first across its groups (deal.h).
 
 #include "launch.h"
 #include "deal.h"
@@ -906,8 +909,8 @@ hipError_t launch_pipe(const PrefillArgs& a, hipStream_t stream) {
     if (c2 == 0.f) c2 = 1e-30f;
     int ps_log2 = 0;
     while ((1 << ps_log2) < a.page_size) ++ps_log2;
-    // one round of causal items, one run of whole groups per XCD: balance the
-    // CUs by weight (four waves: two workgroups per CU, eight waves: one)
+    // causal items, one run of whole groups per XCD: order by weight (four
+    // waves: two workgroups per CU, eight waves: one)
     const int pair = PAGED ? 0
                            : balance_arg(nitems, deal.chunk, (long long)(a.Hq / a.Hkv) * nqt, deal.grid, a.causal,
                                          a.num_cu, NW == 4 ? 2 : 1);
@@ -924,7 +927,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     const long long nitems = (long long)a.B * a.Hq * nqt;
     const Deal deal = make_deal(nitems, (long long)(a.Hq / a.Hkv) * nqt, a.Hq / a.Hkv, PAGED);
     if (deal.grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    // one round of causal items (three workgroups per CU): balance the CUs
+    // causal items: order by weight (three workgroups per CU)
     const int pair = PAGED ? 0
                            : balance_arg(nitems, deal.chunk, (long long)(a.Hq / a.Hkv) * nqt, deal.grid, a.causal,
                                          a.num_cu, 3);

@@ -122,3 +122,27 @@ def test_full_size_workload_head_groups():
         check_grad(f64(dq[b:b + 1, hs]), want[0], f"dq b={b} g={g}")
         check_grad(f64(dk[b:b + 1, g:g + 1]), want[1], f"dk b={b} g={g}")
         check_grad(f64(dv[b:b + 1, g:g + 1]), want[2], f"dv b={b} g={g}")
+
+
+def test_weight_ordered_rounds_head_groups():
+    # more dQ items (128-row query tiles) than workgroup slots, in groups of
+    # one head: each XCD takes its items heaviest query tile first
+    B, Hq, Hkv, S, D = 4, 16, 16, 2048, 128
+    say(f"backward weight-ordered rounds B={B} Hq={Hq} S={S} D={D}")
+    q, k, v = inputs.prefill_inputs(B, Hq, Hkv, S, S, D, "bf16", 62)
+    do = torch.randn((B, Hq, S, D), generator=torch.Generator().manual_seed(63)).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(D)
+    qd, kd, vd, dod = cuda(q, k, v, do)
+    o, lse = attn.fwd_lse(qd, kd, vd, scale=scale, causal=True)
+    # outputs start as NaN: an item that no workgroup took leaves them so
+    outs = [torch.full_like(t, float("nan")) for t in (qd, kd, vd)]
+    attn.bwd(qd, kd, vd, o, dod, lse, scale=scale, causal=True, dq=outs[0], dk=outs[1], dv=outs[2])
+    torch.cuda.synchronize()
+    dq, dk, dv = (t.cpu() for t in outs)
+    assert all(torch.isfinite(t.float()).all() for t in (dq, dk, dv))
+    for b, h in [(0, 0), (B - 1, Hq - 1), (2, 7)]:
+        say(f"  oracle on batch {b}, head {h}")
+        s = (slice(b, b + 1), slice(h, h + 1))
+        want = oracle.attention_bwd(f64(q[s]), f64(k[s]), f64(v[s]), f64(do[s]), scale, True, 0, row_chunk=1024)
+        for name, g, w in zip(("dq", "dk", "dv"), (dq[s], dk[s], dv[s]), want):
+            check_grad(f64(g), w, f"{name} b={b} h={h}")

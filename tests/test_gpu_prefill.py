@@ -85,6 +85,31 @@ def test_full_size_workload_sampled_rows(name):
     assert torch.isfinite(got.float()).all()
 
 
+# More causal items than workgroup slots, in (batch, kv head) groups too small
+# to fill two dispatch rounds of an XCD: each XCD then takes its items heaviest
+# query tile first across its groups. One shape per kernel (D = 64; D = 128 with
+# four waves for at most 2048 keys, eight waves beyond). The output starts as
+# NaN, so a work item that no workgroup took leaves non-finite rows.
+@pytest.mark.parametrize("shape", [(16, 12, 12, 1024, 64), (12, 32, 8, 1024, 128), (2, 16, 16, 4096, 128)])
+def test_weight_ordered_rounds_sampled_rows(shape):
+    B, Hq, Hkv, S, D = shape
+    say(f"prefill weight-ordered rounds B={B} Hq={Hq} Hkv={Hkv} S={S} D={D}")
+    q, k, v = inputs.prefill_inputs(B, Hq, Hkv, S, S, D, "bf16", 61)
+    scale = 1.0 / math.sqrt(D)
+    qd, kd, vd = cuda(q, k, v)
+    o = torch.full_like(qd, float("nan"))
+    attn.fwd(qd, kd, vd, o=o, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    got = o.cpu()
+    assert torch.isfinite(got.float()).all()
+    qn, kn, vn = (t.float().numpy() for t in (q, k, v))
+    rng = np.random.default_rng(1)
+    for b, h in [(0, 0), (B - 1, Hq - 1), (B // 2, Hq // 2), (B - 1, 1)]:
+        rows = _sampled_rows(S, rng)
+        want = oracle.attention_rows(qn, kn, vn, b, h, rows, scale, True, 0)
+        check_bf16(f64(got[b, h][rows]), want, f"b={b} h={h}")
+
+
 # ---- ragged and small shapes ---------------------------------------------------
 
 SHAPES = [
