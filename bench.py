@@ -48,15 +48,26 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def _kernel_sha256(source_file):
+    """SHA-256 over a kernel source followed by every header beside it (the
+    work deal and launch arguments live there), in name order."""
+    d = os.path.dirname(source_file)
+    h = hashlib.sha256()
+    for path in [source_file] + sorted(os.path.join(d, n) for n in os.listdir(d) if n.endswith(".h")):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def _traffic(kernel_key, source_file):
     """HBM bytes per launch from the committed PMC summary, if the kernel's
-    source is unchanged since those counters were taken; else None."""
+    source and headers are unchanged since those counters were taken; else
+    None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)[kernel_key]
-        with open(source_file, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = _kernel_sha256(source_file)
     except (OSError, KeyError, ValueError):
         return None
     if rec.get("source_sha256") != sha:
