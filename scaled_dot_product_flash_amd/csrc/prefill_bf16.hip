@@ -389,28 +389,38 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         if (t + 1 < t_end) step(t + 1, k_lds1, v_lds1, k_lds0, v_lds0);
     }
 
-    // ---- epilogue: O = O^T / l, bf16, 4 consecutive d per 8-byte store -----
-    if (!wave_rows || qrow >= Sq) return;
+    // ---- epilogue: O = O^T / l in bf16, through LDS to whole-row stores ----
+    if (!wave_rows) return;
     const float l_tot = l_run + xor32(l_run);
     const float inv = 1.f / l_tot;
     // log-sum-exp of the scaled logits, natural log: sum_j exp(scale s_j)
     // = 2^m_ref * l with m_ref the reference maximum in log2 units
-    if (LSE != nullptr && hh == 0)
+    if (LSE != nullptr && hh == 0 && qrow < Sq)
         LSE[((size_t)b * Hq + h) * Sq + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
-    uint16_t* op = O + qo_base + (size_t)qrow * D;
+    // The wave's 32 x D block (half a K/V tile buffer, free after the last
+    // barrier) is written in the accumulator layout, 8 bytes per (row, four
+    // d), and read back as whole rows, so each store instruction writes
+    // 64 / CPR contiguous rows. 16-byte chunks are XOR-swizzled by row.
+    unsigned char* stage = ((wave >> 1) == 0 ? k_lds0 : v_lds0) + (wave & 1) * (32 * D * 2);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             f32x2 a = {oacc[db][4 * r + 0] * inv, oacc[db][4 * r + 1] * inv};
             f32x2 c = {oacc[db][4 * r + 2] * inv, oacc[db][4 * r + 3] * inv};
-            bf16x2 x = __builtin_convertvector(a, bf16x2);
-            bf16x2 y = __builtin_convertvector(c, bf16x2);
             uint2 st;
-            st.x = __builtin_bit_cast(uint32_t, x);
-            st.y = __builtin_bit_cast(uint32_t, y);
-            *reinterpret_cast<uint2*>(op + 32 * db + 8 * r + 4 * hh) = st;
+            st.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2));
+            st.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(c, bf16x2));
+            const int chunk = (4 * db + r) ^ (ln & (CPR - 1));
+            *reinterpret_cast<uint2*>(stage + ln * (D * 2) + chunk * 16 + hh * 8) = st;
         }
+    const int cl = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < CPR / 2; ++i) {
+        const int row = i * (64 / CPR) + lane / CPR;
+        const uint4 x = *reinterpret_cast<const uint4*>(stage + row * (D * 2) + ((cl ^ (row & (CPR - 1))) << 4));
+        if (wr0 + row < Sq) *reinterpret_cast<uint4*>(O + qo_base + (size_t)(wr0 + row) * D + 8 * cl) = x;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -548,15 +558,6 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     const int qrow = wr0 + ln;
     const int qpos = qrow + off;
     bf16x8 qreg[DS];
-    {
-        const bool ok = qrow < Sq;
-        const uint16_t* qp = Q + qo_base + (size_t)(ok ? qrow : 0) * D + 8 * hh;
-#pragma unroll
-        for (int st = 0; st < DS; ++st) {
-            uint4 x = ok ? ld_global16(qp + 16 * st) : make_uint4(0, 0, 0, 0);
-            qreg[st] = as_bf16x8(x);
-        }
-    }
 
     // K rows keep their 16-byte chunks XOR-swizzled by (row & 15), V rows by
     // (row & 3) << 2; the DMA realises the swizzle through the source offset
@@ -838,6 +839,16 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     // exact zeros.
     f32x16 sA[KB], sB[KB];
     issue(krs, t_begin, k_lds0, false);
+    // Q rows into registers, queued behind the first K tile's DMA
+    {
+        const bool ok = qrow < Sq;
+        const uint16_t* qp = Q + qo_base + (size_t)(ok ? qrow : 0) * D + 8 * hh;
+#pragma unroll
+        for (int st = 0; st < DS; ++st) {
+            uint4 x = ok ? ld_global16(qp + 16 * st) : make_uint4(0, 0, 0, 0);
+            qreg[st] = as_bf16x8(x);
+        }
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (t_begin + 1 < t_end) issue(krs, t_begin + 1, k_lds1, false);
@@ -878,14 +889,20 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     }
     for (; t < t_end; ++t) idle_step(t);
 
-    if (qrow >= Sq) return;
+    if (wr0 >= Sq) return;
     const float2 lh = halves(l_run);
     const float inv = 1.f / (lh.x + lh.y);
     // log-sum-exp of the scaled logits, natural log: sum_j exp(scale s_j)
     // = 2^m_ref * l with m_ref the reference maximum in log2 units
-    if (LSE != nullptr && hh == 0)
+    if (LSE != nullptr && hh == 0 && qrow < Sq)
         LSE[((size_t)b * Hq + h) * Sq + qrow] = (m_run + __log2f(lh.x + lh.y)) * 0.69314718055994531f;
-    uint16_t* op = O + qo_base + (size_t)qrow * D;
+    // The wave's 32 x D output block goes out through LDS (the K/V buffers
+    // are free after the last barrier; 8 KiB per wave): from the accumulator
+    // layout (per 16-byte column chunk, 16 bytes of each of 32 rows) to
+    // whole rows, so every store instruction writes four contiguous rows.
+    // Chunks are XOR-swizzled by (row & 15) so both sides spread over banks.
+    unsigned char* stage = (wave >> 1) == 0 ? k_lds0 : (wave >> 1) == 1 ? k_lds1 : (wave >> 1) == 2 ? v_lds0 : v_lds1;
+    stage += (wave & 1) * (32 * D * 2);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -895,8 +912,16 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             uint2 st;
             st.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2));
             st.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(c, bf16x2));
-            *reinterpret_cast<uint2*>(op + 32 * db + 8 * r + 4 * hh) = st;
+            const int chunk = (4 * db + r) ^ (ln & (CPR - 1));
+            *reinterpret_cast<uint2*>(stage + ln * (D * 2) + chunk * 16 + hh * 8) = st;
         }
+    const int cl = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < CPR / 2; ++i) {
+        const int row = i * (64 / CPR) + lane / CPR;
+        const uint4 x = *reinterpret_cast<const uint4*>(stage + row * (D * 2) + ((cl ^ (row & (CPR - 1))) << 4));
+        if (wr0 + row < Sq) *reinterpret_cast<uint4*>(O + qo_base + (size_t)(wr0 + row) * D + 8 * cl) = x;
+    }
 }
 
 template <int NW, bool NEG, bool PAGED>
