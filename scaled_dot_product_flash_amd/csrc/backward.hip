@@ -141,6 +141,32 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
     return r;
 }
 
+// Stores a wave's 32 x D bf16 block, given in the 32x32 MFMA accumulator
+// layout (lane ln + 32 hh: row ln, d = 32 db + 8 r + 4 hh .. +3 as the word
+// w[db][r]), as rows r0 .. r0 + 31 of a [rows, D] slice, skipping rows at or
+// past `nrows`. The block passes through the wave's own 32 x D region of LDS,
+// 16-byte chunks XOR-swizzled by row, so that each store instruction writes
+// 64 / (D / 8) whole rows instead of 16 bytes of each of 32 rows.
+template <int D>
+__device__ __forceinline__ void store_block(unsigned char* stage, const uint2 (&w)[D / 32][4], uint16_t* out, int r0,
+                                            int nrows, int lane) {
+    constexpr int CPR = D / 8;   // 16-byte chunks per row
+    const int ln = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            *reinterpret_cast<uint2*>(stage + ln * (D * 2) + (((4 * db + r) ^ (ln & (CPR - 1))) << 4) + hh * 8) =
+                w[db][r];
+    const int cl = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < CPR / 2; ++i) {
+        const int row = i * (64 / CPR) + lane / CPR;
+        const uint4 x = *reinterpret_cast<const uint4*>(stage + row * (D * 2) + ((cl ^ (row & (CPR - 1))) << 4));
+        if (r0 + row < nrows) *reinterpret_cast<uint4*>(out + (size_t)(r0 + row) * D + 8 * cl) = x;
+    }
+}
+
 // 8 values of a 32x32 accumulator (k step `c` of its rows) as a bf16 operand
 __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int c) {
     bf16x8 r;
@@ -353,15 +379,17 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         }
     }
 
-    if (!row_ok) return;
-    uint16_t* out = dQ + qo_base + (size_t)qrow * D;
+    // dQ through half a K tile buffer (free after the last barrier)
+    if (!wave_rows) return;
+    uint2 wq[DB][4];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            *reinterpret_cast<uint2*>(out + 32 * db + 8 * r + 4 * hh) =
-                pack4(dq[db][4 * r] * scale, dq[db][4 * r + 1] * scale, dq[db][4 * r + 2] * scale,
-                      dq[db][4 * r + 3] * scale);
+            wq[db][r] = pack4(dq[db][4 * r] * scale, dq[db][4 * r + 1] * scale, dq[db][4 * r + 2] * scale,
+                              dq[db][4 * r + 3] * scale);
+    store_block<D>(((wave >> 1) == 0 ? k_lds0 : k_lds1) + (wave & 1) * (32 * D * 2), wq, dQ + qo_base, wr0, Sq,
+                   lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -685,8 +713,9 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     }
 
     // accumulator value v of block db holds d = 32 db + 8(v/4) + 4hh + v%4
-    if (!key_ok) return;
+    if (!wave_keys) return;
     if (part != nullptr) {
+        if (!key_ok) return;
         const size_t plane = (size_t)nbg * Sk * D;
         float* kp = part + (size_t)split * plane + ((size_t)bg * Sk + key) * D;
         float* vp = part + (size_t)(nsplit + split) * plane + ((size_t)bg * Sk + key) * D;
@@ -702,18 +731,19 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             }
         return;
     }
-    uint16_t* kout = dK + kv_base + (size_t)key * D;
-    uint16_t* vout = dV + kv_base + (size_t)key * D;
+    // dK, then dV, through the wave's own V rows in LDS (no longer needed)
+    uint2 wk[DB][4], wv[DB][4];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int d = 32 * db + 8 * r + 4 * hh;
-            *reinterpret_cast<uint2*>(kout + d) = pack4(dk[db][4 * r] * scale, dk[db][4 * r + 1] * scale,
-                                                        dk[db][4 * r + 2] * scale, dk[db][4 * r + 3] * scale);
-            *reinterpret_cast<uint2*>(vout + d) =
-                pack4(dv[db][4 * r], dv[db][4 * r + 1], dv[db][4 * r + 2], dv[db][4 * r + 3]);
+            wk[db][r] = pack4(dk[db][4 * r] * scale, dk[db][4 * r + 1] * scale, dk[db][4 * r + 2] * scale,
+                              dk[db][4 * r + 3] * scale);
+            wv[db][r] = pack4(dv[db][4 * r], dv[db][4 * r + 1], dv[db][4 * r + 2], dv[db][4 * r + 3]);
         }
+    unsigned char* stage = v_lds + wave * (32 * D * 2);
+    store_block<D>(stage, wk, dK + kv_base, kw0, Sk, lane);
+    store_block<D>(stage, wv, dV + kv_base, kw0, Sk, lane);
 }
 
 // dK, dV of a split key block: the sum, in split order, of the runs' float32
