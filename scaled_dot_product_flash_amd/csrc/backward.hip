@@ -715,8 +715,39 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     // accumulator value v of block db holds d = 32 db + 8(v/4) + 4hh + v%4
     if (!wave_keys) return;
     if (part != nullptr) {
-        if (!key_ok) return;
         const size_t plane = (size_t)nbg * Sk * D;
+        if constexpr (D == 128) {
+            // float partials, 64 columns (two d blocks, 256 bytes of a row)
+            // per pass through the wave's 8 KiB of V rows in LDS, read back
+            // as whole 256-byte row segments, four rows per store instruction
+            unsigned char* stage = v_lds + wave * (32 * D * 2);
+            const int cl = lane & 15;
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                float* base = part + (size_t)(m * nsplit + split) * plane + ((size_t)bg * Sk + kw0) * D;
+#pragma unroll
+                for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+                    for (int x = 0; x < 2; ++x)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const f32x16& acc = m == 0 ? dk[2 * pass + x] : dv[2 * pass + x];
+                            const float s = m == 0 ? scale : 1.f;
+                            const int chunk = (8 * x + 2 * r + hh) ^ (ln & 15);
+                            *reinterpret_cast<float4*>(stage + ln * 256 + chunk * 16) =
+                                make_float4(acc[4 * r] * s, acc[4 * r + 1] * s, acc[4 * r + 2] * s, acc[4 * r + 3] * s);
+                        }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int row = 4 * i + (lane >> 4);
+                        const float4 v4 = *reinterpret_cast<const float4*>(stage + row * 256 + ((cl ^ (row & 15)) << 4));
+                        if (kw0 + row < Sk) *reinterpret_cast<float4*>(base + (size_t)row * D + 64 * pass + 4 * cl) = v4;
+                    }
+                }
+            }
+            return;
+        }
+        if (!key_ok) return;
         float* kp = part + (size_t)split * plane + ((size_t)bg * Sk + key) * D;
         float* vp = part + (size_t)(nsplit + split) * plane + ((size_t)bg * Sk + key) * D;
 #pragma unroll
