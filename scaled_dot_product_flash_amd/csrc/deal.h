@@ -26,11 +26,11 @@ constexpr int kXcds = 8;   // XCDs of an MI355X; workgroup w is dispatched to XC
 //  * bal < 0 (several rounds): slot s takes rank s, so the dispatcher, which
 //    gives the next slot to the first CU that frees up, runs the XCD's
 //    heaviest items first and ends on its lightest.
-__device__ __forceinline__ int dealt_item(int w, int chunk, int nitems, int bal, int nqt, int G) {
+__host__ __device__ __forceinline__ int dealt_item(int w, int chunk, int nitems, int bal, int nqt, int G) {
     const int x = w % kXcds;
     const int s = w / kXcds;
     if (bal != 0) {
-        const int n = min(chunk, nitems - x * chunk);   // this XCD's items: whole groups
+        const int n = nitems - x * chunk < chunk ? nitems - x * chunk : chunk;   // this XCD's items: whole groups
         if (s >= n) return -1;
         int rank = s;
         if (bal > 0) {
