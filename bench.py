@@ -19,8 +19,12 @@ chunked prefill (512 new tokens per sequence) against a paged cache;
 append of one new token per sequence to the same cache; ``backward`` times the
 backward pass (dQ, dK, dV) on the prefill shape at 10·D flop per visible pair;
 ``other_prefill`` times the float32 128-token, GPT-2-sized causal and 16k
-sliding-window prefill configurations. ``cpu_baseline`` times the
-float64 oracle on a bounded sample of the prefill workload on the host cores.
+sliding-window prefill configurations. ``cpu_baseline`` times the float64
+oracle over the whole prefill workload and the whole decode workload on the
+host cores (a pool of single-threaded worker processes, at most 16).
+Before the warmup, the step runs back to back for ``--settle-ms`` so that no
+timed step sees the clock ramp of an idle GPU; the headline is the median
+launch, with mean, standard deviation and minimum beside it.
 Progress goes to stderr.
 """
 
@@ -42,6 +46,8 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 PREFILL = "gqa_causal_4k"
 DECODE = "paged_decode"
 WINDOW = 4096               # sliding-window decode measured beside the step
+TRAFFIC_SOURCE = ("profiles/traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE per dispatch, scaled by a plain copy, "
+                  "taken on the kernel source whose sha256 it records (null when the source has changed since)")
 
 
 def log(msg):
@@ -75,44 +81,110 @@ def _traffic(kernel_key, source_file):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(q, k, v, scale, seconds):
-    """Time the float64 oracle on whole (batch, head) units of the prefill
-    workload until `seconds` have passed; report TFLOP/s on the same
-    visible-pair count the GPU figure uses."""
+# ---- CPU baseline: the float64 oracle in a pool of single-threaded workers ----
+# The pool is forked before the GPU is touched, with the inputs already in
+# module globals (shared copy-on-write); each worker limits BLAS to one thread.
+
+_CPU = {}
+
+
+def _cpu_worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _cpu_prefill_unit(bh):
     import numpy as np
 
     import oracle
-    from scaled_dot_product_flash_amd import work
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = 1
-    qn, kn, vn = (t.float().numpy() for t in (q, k, v))
-    B, Hq, Sq, D = qn.shape
-    Sk = kn.shape[2]
-    units = [(b, h) for b in range(B) for h in range(Hq)]
-    np.random.default_rng(0).shuffle(units)
-    rows = np.arange(Sq)
-    per_unit = work.attention_flops(work.visible_pairs(Sq, Sk, True, 0), D)
-    done = 0
+    b, h = bh
+    c = _CPU["prefill"]
     t0 = time.perf_counter()
-    for b, h in units:
-        out = oracle.attention_rows(qn, kn, vn, b, h, rows, scale, True, 0)
-        assert np.isfinite(out).all()
-        done += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    el = time.perf_counter() - t0
+    out = oracle.attention_rows(c["q"], c["k"], c["v"], b, h, np.arange(c["q"].shape[2]), c["scale"], True, 0)
+    assert np.isfinite(out).all()
+    return time.perf_counter() - t0
+
+
+def _cpu_decode_seq(b):
+    import numpy as np
+
+    import oracle
+
+    c = _CPU["decode"]
+    first, count = int(c["first"][b]), int(c["count"][b])
+    t0 = time.perf_counter()
+    out = oracle.decode_paged(c["q"][b:b + 1], c["k_pool"], c["v_pool"], c["page_table"][first:first + count],
+                              c["seq_lens"][b:b + 1], c["page_size"], c["scale"])
+    assert np.isfinite(out).all()
+    return time.perf_counter() - t0
+
+
+def cpu_workers():
+    """Worker count: the host cores this process may run on, at most 16 (one
+    GPU's share of a GPU host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_prepare(q, k, v, p_scale, dd, d_scale, page_size):
+    """Float32 copies (the exact bf16 values) of both workloads for the oracle
+    workers, then the fork of the worker pool."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    _CPU["prefill"] = {"q": q.float().numpy(), "k": k.float().numpy(), "v": v.float().numpy(), "scale": p_scale}
+    lens = dd["seq_lens"].numpy().astype(np.int64)
+    count = (lens + page_size - 1) // page_size
+    _CPU["decode"] = {"q": dd["q"].float().numpy(), "k_pool": dd["k_pool"].float().numpy(),
+                      "v_pool": dd["v_pool"].float().numpy(), "page_table": dd["page_table"].numpy(),
+                      "seq_lens": dd["seq_lens"].numpy(), "first": np.concatenate([[0], np.cumsum(count)[:-1]]),
+                      "count": count, "page_size": page_size, "scale": d_scale}
+    n = cpu_workers()
+    return mp.get_context("fork").Pool(n, initializer=_cpu_worker_init), n
+
+
+def cpu_baseline(pool, n, p_flops, d_bytes):
+    """Time the float64 oracle over the whole prefill workload (every
+    (batch, query head), all query rows) and the whole decode workload (every
+    sequence), spread over the worker pool; report TFLOP/s and GB/s on the
+    algorithmic counts the GPU figures use."""
+    import random
+
+    c = _CPU["prefill"]
+    B, Hq = c["q"].shape[:2]
+    units = [(b, h) for b in range(B) for h in range(Hq)]
+    random.Random(0).shuffle(units)
+    pool.map(time.sleep, [0.05] * n)          # every worker started
+    t0 = time.perf_counter()
+    unit_s = pool.map(_cpu_prefill_unit, units, chunksize=1)
+    p_wall = time.perf_counter() - t0
+    nseq = len(_CPU["decode"]["seq_lens"])
+    seqs = list(range(nseq))
+    random.Random(1).shuffle(seqs)
+    t0 = time.perf_counter()
+    seq_s = pool.map(_cpu_decode_seq, seqs, chunksize=1)
+    d_wall = time.perf_counter() - t0
+    pool.close()
+    pool.join()
     return {
-        "value": round(done * per_unit / el / 1e12, 6),
+        "value": round(p_flops / p_wall / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": n,
         "kind": "oracle",
-        "sample": f"{done} of {len(units)} (batch, query head) units of the causal GQA prefill workload, "
-                  f"all {Sq} query rows each, float64 numpy, {el:.1f} s",
+        "sample": f"the whole causal GQA prefill workload: all {len(units)} (batch, query head) units, every query "
+                  f"row, float64 numpy, {n} single-threaded worker processes, {p_wall:.2f} s wall "
+                  f"({sum(unit_s):.1f} s of worker time)",
+        "decode": {
+            "value": round(d_bytes / d_wall / 1e9, 4),
+            "unit": "GB/s",
+            "sample": f"the whole paged decode workload: all {nseq} sequences, float64 numpy, {n} single-threaded "
+                      f"worker processes, {d_wall:.2f} s wall ({sum(seq_s):.1f} s of worker time)",
+        },
     }
 
 
@@ -122,8 +194,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100,
                     help="untimed steps first; the GPU takes ~50 ms of sustained load to reach its steady clocks")
+    ap.add_argument("--settle-ms", type=float, default=500.0,
+                    help="untimed steps run back to back for this long before the warmup, so the GPU reaches its "
+                         "sustained clocks before any timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="add one plain 256 MiB device copy per step (byte-counter scale for PMC runs)")
     args = ap.parse_args()
@@ -139,23 +213,30 @@ def main():
     import scaled_dot_product_flash_amd as attn
     from scaled_dot_product_flash_amd import inputs, work
 
+    wp, wd = inputs.WORKLOADS[PREFILL], inputs.WORKLOADS[DECODE]
+    log("generating inputs")
+    q, k, v = inputs.workload_inputs(PREFILL)
+    dd = inputs.workload_inputs(DECODE)
+    p_scale = 1.0 / math.sqrt(wp["D"])
+    d_scale = 1.0 / math.sqrt(wd["D"])
+    pool = None
+    if not args.no_cpu_baseline:
+        # forked before anything touches the GPU
+        pool, n_workers = cpu_prepare(q, k, v, p_scale, dd, d_scale, wd["page_size"])
+
     if not torch.cuda.is_available():
+        if pool is not None:
+            pool.terminate()
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     attn.load_library()
 
-    wp, wd = inputs.WORKLOADS[PREFILL], inputs.WORKLOADS[DECODE]
-    log("generating inputs")
-    q, k, v = inputs.workload_inputs(PREFILL)
-    dd = inputs.workload_inputs(DECODE)
     pq, pk, pv = (t.to(dev) for t in (q, k, v))
     po = torch.empty_like(pq)
     dq, dkp, dvp, dpt, dsl = (dd[n].to(dev) for n in ("q", "k_pool", "v_pool", "page_table", "seq_lens"))
     do = torch.empty_like(dq)
-    p_scale = 1.0 / math.sqrt(wp["D"])
-    d_scale = 1.0 / math.sqrt(wd["D"])
     if args.copy_calibration:
         csrc = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         cdst = torch.empty_like(csrc)
@@ -173,6 +254,19 @@ def main():
         if args.copy_calibration:
             cdst.copy_(csrc)
 
+    # settle: the same step back to back until the GPU has run under load for
+    # settle_ms (its clocks take tens of ms of sustained load to level off)
+    log(f"settle {args.settle_ms:.0f} ms")
+    settle_steps = 0
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(10):
+            step()
+        settle_steps += 10
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= args.settle_ms:
+            break
+    settle_ms = (time.perf_counter() - t0) * 1e3
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -315,10 +409,16 @@ def main():
 
     p_flops = work.prefill_flops(wp["B"], wp["Hq"], wp["Sq"], wp["Sk"], wp["D"], True, 0)
     d_bytes = work.decode_kv_bytes(dd["seq_lens"].tolist(), wd["Hkv"], wd["D"], 2)
-    p_mean = statistics.fmean(pre_ms)
-    d_mean = statistics.fmean(dec_ms)
-    p_tflops = p_flops / (p_mean * 1e-3) / 1e12
-    d_gbps = d_bytes / (d_mean * 1e-3) / 1e9
+    p_mean, p_med = statistics.fmean(pre_ms), statistics.median(pre_ms)
+    d_mean, d_med = statistics.fmean(dec_ms), statistics.median(dec_ms)
+    p_std = statistics.stdev(pre_ms) if len(pre_ms) > 1 else 0.0
+    d_std = statistics.stdev(dec_ms) if len(dec_ms) > 1 else 0.0
+    # headline: the median launch; the roofline uses the mean launch duration
+    # (what a kernel trace averages)
+    p_tflops = p_flops / (p_med * 1e-3) / 1e12
+    d_gbps = d_bytes / (d_med * 1e-3) / 1e9
+    p_tflops_mean = p_flops / (p_mean * 1e-3) / 1e12
+    d_gbps_mean = d_bytes / (d_mean * 1e-3) / 1e9
     csrc_dir = os.path.join(ROOT, "scaled_dot_product_flash_amd", "csrc")
 
     out = {
@@ -328,6 +428,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": round(settle_ms, 1),
+        "settle_steps": settle_steps,
         "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -344,30 +446,35 @@ def main():
                        "kv_bytes_per_call": d_bytes},
             "parallelism": "single GPU",
         },
-        "prefill": {"ms_mean": round(p_mean, 5), "ms_median": round(statistics.median(pre_ms), 5),
+        "prefill": {"ms_median": round(p_med, 5), "ms_mean": round(p_mean, 5), "ms_std": round(p_std, 5),
                     "ms_min": round(min(pre_ms), 5), "tflops": round(p_tflops, 3),
-                    "frac_peak": round(p_tflops / PEAK_BF16_TFLOPS, 4)},
+                    "tflops_at_mean": round(p_tflops_mean, 3), "frac_peak": round(p_tflops / PEAK_BF16_TFLOPS, 4)},
         "roofline": {
             "bound": "mfma",
-            "achieved": round(p_tflops, 3),
+            "achieved": round(p_tflops_mean, 3),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
+            "frac": round(p_tflops_mean / PEAK_BF16_TFLOPS, 4),
             "traffic": _traffic("prefill_pipe_kernel", os.path.join(csrc_dir, "prefill_bf16.hip")),
+            "achieved_from": "algorithmic flop per launch / mean launch duration (HIP events on the launch stream)",
+            "traffic_source": TRAFFIC_SOURCE,
         },
         "decode": {
             "value": round(d_gbps, 2),
             "unit": "GB/s",
+            "ms_median": round(d_med, 5),
             "ms_mean": round(d_mean, 5),
-            "ms_median": round(statistics.median(dec_ms), 5),
+            "ms_std": round(d_std, 5),
             "ms_min": round(min(dec_ms), 5),
             "roofline": {
                 "bound": "hbm",
-                "achieved": round(d_gbps, 2),
+                "achieved": round(d_gbps_mean, 2),
                 "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s",
-                "frac": round(d_gbps / PEAK_HBM_GBPS, 4),
+                "frac": round(d_gbps_mean / PEAK_HBM_GBPS, 4),
                 "traffic": _traffic("decode_split_kernel", os.path.join(csrc_dir, "decode_paged.hip")),
+                "achieved_from": "KV bytes per call / mean duration of the call (split and merge kernels)",
+                "traffic_source": TRAFFIC_SOURCE,
             },
         },
     }
@@ -411,9 +518,9 @@ def main():
         "kernels": "bwd_dq_kernel then bwd_dkdv_kernel; scores and dP are computed in both (14*D executed)",
     }
     out["other_prefill"] = other
-    if not args.no_cpu_baseline:
-        log(f"cpu baseline (~{args.cpu_seconds:.0f} s of oracle work)")
-        out["cpu_baseline"] = cpu_baseline(q, k, v, p_scale, args.cpu_seconds)
+    if pool is not None:
+        log(f"cpu baseline: the float64 oracle over both workloads, {n_workers} worker processes")
+        out["cpu_baseline"] = cpu_baseline(pool, n_workers, p_flops, d_bytes)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

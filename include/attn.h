@@ -28,10 +28,17 @@
  *   - A zero batch (B == 0), or Sq == 0 for prefill, is a valid empty call.
  *   - Graph capture: a call enqueues kernels only (no memset, copy or host
  *     synchronisation). The one allocation is the workspace of the decode and
- *     backward calls, kept per (device, stream) and grown on demand (growing
- *     synchronises the stream and frees the old buffer). To capture those
- *     calls in a HIP graph, run them once on the capture stream with the
- *     largest shapes to be captured; the graph then reuses that workspace.
+ *     backward calls, kept per (device, stream) and grown on demand. A buffer
+ *     that a larger request replaces is retired, not freed, so kernels still
+ *     in flight and graphs that captured an earlier call keep a valid buffer
+ *     until attn_release. The workspace never grows while `stream` is being
+ *     captured (ATTN_ERR_CAPTURE): run the calls once on the capture stream
+ *     with the largest shapes to be captured first. A graph that captured a
+ *     decode or backward call must not be replayed after attn_release.
+ *   - Threads: every entry point may be called from several host threads.
+ *     The workspace lock is held from its size check until the call's
+ *     kernels are enqueued; two calls that share a (device, stream) run in
+ *     the order they were enqueued.
  */
 #ifndef ATTN_H
 #define ATTN_H
@@ -61,7 +68,9 @@ enum {
     ATTN_ERR_NOMEM = -9,    /* the decode workspace could not be allocated */
     ATTN_ERR_HIP = -10,     /* a HIP runtime call or kernel launch failed */
     ATTN_ERR_FULL = -11,    /* the page pool has too few free pages */
-    ATTN_ERR_SEQ = -12      /* a sequence id the page pool does not hold */
+    ATTN_ERR_SEQ = -12,     /* a sequence id the page pool does not hold */
+    ATTN_ERR_CAPTURE = -13  /* the decode/backward workspace would have to grow
+                               while `stream` is being captured into a graph */
 };
 
 /*
@@ -172,6 +181,11 @@ int attn_fwd_paged(const void* q, const void* k_pool, const void* v_pool,
  *   allocated on first use per (device, stream) and grown as needed; calls on
  *   different streams never share a workspace. P is rounded to bfloat16
  *   before P·V, as in attn_fwd.
+ *   Errors: NULL; SHAPE (B < 0, B > 65535, Hq > 65535 or B * Hq > 2^24: the
+ *   launch grids index sequences and head groups in 16-bit grid dimensions
+ *   and the merge runs one workgroup per (sequence, query head)); HEADS;
+ *   HEADDIM; PAGE; SCALE; ALIGN (16 bytes for tensors, 4 for the int32
+ *   arrays); NOMEM and CAPTURE for the workspace; HIP. B == 0 is a no-op.
  */
 int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                       const int32_t* page_table, const int32_t* seq_lens,

@@ -10,6 +10,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 namespace {
 
@@ -50,7 +51,13 @@ int validate_prefill(const void* q, const void* k, const void* v, const void* o,
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
-// ---- decode workspace: one buffer per (device, stream), grown on demand ----
+// ---- workspace of the decode and backward calls ----------------------------
+// One buffer per (device, stream), grown on demand. A buffer that a larger
+// request replaces is retired, not freed: kernels already enqueued on the
+// stream, and HIP graphs that captured a call, keep using it, so it stays
+// allocated until attn_release. The mutex is held from the size check until
+// the call's kernels are enqueued, so no other host thread can replace the
+// buffer in between.
 
 struct Workspace {
     float* ptr = nullptr;
@@ -59,21 +66,22 @@ struct Workspace {
 
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::vector<std::pair<int, void*>> g_retired;   // (device, buffer) freed by attn_release
 std::map<int, int> g_cu_count;
 
+// Caller holds g_ws_mutex.
 int get_workspace(int device, hipStream_t stream, size_t floats, float** out) {
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace& w = g_ws[{device, stream}];
     if (w.floats < floats) {
-        if (w.ptr) {
-            // earlier calls on this stream may still read the old buffer
-            if (hipStreamSynchronize(stream) != hipSuccess) return ATTN_ERR_HIP;
-            if (hipFree(w.ptr) != hipSuccess) return ATTN_ERR_HIP;
-            w.ptr = nullptr;
-            w.floats = 0;
-        }
+        // growing under stream capture would leave the graph with a buffer
+        // that the next eager growth could replace; the caller must size the
+        // workspace with an eager call first
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return ATTN_ERR_HIP;
+        if (cs != hipStreamCaptureStatusNone) return ATTN_ERR_CAPTURE;
         void* p = nullptr;
         if (hipMalloc(&p, floats * sizeof(float)) != hipSuccess || !p) return ATTN_ERR_NOMEM;
+        if (w.ptr) g_retired.emplace_back(device, w.ptr);
         w.ptr = static_cast<float*>(p);
         w.floats = floats;
     }
@@ -120,7 +128,9 @@ int decode_call(const void* q, const void* k_pool, const void* v_pool, const int
     if (window < 0) return ATTN_ERR_MASK;
     if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
     if (B == 0) return ATTN_OK;
-    if (B > 65535 || Hq > 65535) return ATTN_ERR_SHAPE;
+    // grid dimensions: B and the head groups index workgroups in y and z, and
+    // the merge runs one workgroup per (sequence, query head)
+    if (B > 65535 || Hq > 65535 || (long long)B * Hq > (1LL << 24)) return ATTN_ERR_SHAPE;
     if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !o) return ATTN_ERR_NULL;
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o) || !aligned4(page_table) ||
         !aligned4(seq_lens))
@@ -133,6 +143,7 @@ int decode_call(const void* q, const void* k_pool, const void* v_pool, const int
     if (rc != ATTN_OK) return rc;
     const bool mfma = attn::decode_on_mfma(B, Hq, Hkv, D, ncu);
     const int nsplit = attn::decode_nsplit(B, Hq, Hkv, ncu, mfma);
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
     float* ws = nullptr;
     rc = get_workspace(device, stream, attn::decode_workspace_floats(B, Hq, D, nsplit), &ws);
     if (rc != ATTN_OK) return rc;
@@ -252,6 +263,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     const int crc = cu_count(device, &ncu);
     if (crc != ATTN_OK) return crc;
     const int kv_splits = attn::backward_kv_splits(B, Hkv, Sq, Sk, ncu);
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
     float* ws = nullptr;
     if (Sq > 0) {
         const size_t floats = (attn::backward_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, kv_splits) + 3) / 4;
@@ -279,24 +291,26 @@ const char* attn_strerror(int status) {
         case ATTN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
         case ATTN_ERR_FULL: return "the page pool has too few free pages";
         case ATTN_ERR_SEQ: return "the page pool holds no sequence with this id";
+        case ATTN_ERR_CAPTURE: return "the workspace would have to grow while the stream is being captured";
         default: return "unknown attn status code";
     }
 }
 
 void attn_release(void) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    if (g_ws.empty()) return;
+    if (g_ws.empty() && g_retired.empty()) return;
     int prev = -1;
     const bool have_prev = hipGetDevice(&prev) == hipSuccess;
-    for (auto& kv : g_ws) {
-        if (kv.second.ptr) {
-            if (hipSetDevice(kv.first.first) == hipSuccess) {
-                (void)hipDeviceSynchronize();
-                (void)hipFree(kv.second.ptr);
-            }
+    for (auto& kv : g_ws)
+        if (kv.second.ptr) g_retired.emplace_back(kv.first.first, kv.second.ptr);
+    for (auto& r : g_retired) {
+        if (hipSetDevice(r.first) == hipSuccess) {
+            (void)hipDeviceSynchronize();
+            (void)hipFree(r.second);
         }
     }
     g_ws.clear();
+    g_retired.clear();
     if (have_prev) (void)hipSetDevice(prev);
 }
 

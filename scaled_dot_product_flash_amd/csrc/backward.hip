@@ -158,6 +158,7 @@ __device__ __forceinline__ void store_block(unsigned char* stage, const uint2 (&
         for (int r = 0; r < 4; ++r)
             *reinterpret_cast<uint2*>(stage + ln * (D * 2) + (((4 * db + r) ^ (ln & (CPR - 1))) << 4) + hh * 8) =
                 w[db][r];
+    wave_lds_fence();
     const int cl = lane % CPR;
 #pragma unroll
     for (int i = 0; i < CPR / 2; ++i) {
@@ -165,6 +166,7 @@ __device__ __forceinline__ void store_block(unsigned char* stage, const uint2 (&
         const uint4 x = *reinterpret_cast<const uint4*>(stage + row * (D * 2) + ((cl ^ (row & (CPR - 1))) << 4));
         if (r0 + row < nrows) *reinterpret_cast<uint4*>(out + (size_t)(r0 + row) * D + 8 * cl) = x;
     }
+    wave_lds_fence();   // the region may be written again by the next block
 }
 
 // 8 values of a 32x32 accumulator (k step `c` of its rows) as a bf16 operand
@@ -737,12 +739,14 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                             *reinterpret_cast<float4*>(stage + ln * 256 + chunk * 16) =
                                 make_float4(acc[4 * r] * s, acc[4 * r + 1] * s, acc[4 * r + 2] * s, acc[4 * r + 3] * s);
                         }
+                    wave_lds_fence();
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         const int row = 4 * i + (lane >> 4);
                         const float4 v4 = *reinterpret_cast<const float4*>(stage + row * 256 + ((cl ^ (row & 15)) << 4));
                         if (kw0 + row < Sk) *reinterpret_cast<float4*>(base + (size_t)row * D + 64 * pass + 4 * cl) = v4;
                     }
+                    wave_lds_fence();   // the next pass writes the same region
                 }
             }
             return;

@@ -42,6 +42,10 @@ void kv_append_kernel(const uint16_t* __restrict__ k_new, const uint16_t* __rest
     for (int w = 0; w < kThreads / 64; ++w) off_b += sh_part[w];
 
     const int t = lens[b] - 1;
+    // outside the precondition seq_lens[b] >= 1: there is no position to
+    // write, and t = -1 would address the table entry before the sequence's
+    // own (another sequence's last page)
+    if (t < 0) return;
     const int page = table[off_b + (t >> ps_log2)];
     const size_t dst = (((size_t)page * Hkv) * ps + (size_t)(t & (ps - 1))) * D;  // head 0 of the slot
     const size_t head_stride = (size_t)ps * D;

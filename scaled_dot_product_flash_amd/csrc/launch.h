@@ -8,6 +8,19 @@
 
 namespace attn {
 
+// Orders one wave's LDS accesses across lanes: every lane's accesses before
+// the call come before every lane's accesses after it. The LDS executes a
+// wave's instructions in order, so this only keeps the compiler, which
+// reasons about one lane at a time, from moving an access across it; it
+// emits no instruction. Used where lanes exchange data through LDS (write in
+// one layout, read another lane's values back) and where such a region is
+// written again after it was read.
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 struct PrefillArgs {
     const void* q;
     const void* k;

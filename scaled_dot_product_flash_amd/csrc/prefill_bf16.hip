@@ -414,6 +414,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             const int chunk = (4 * db + r) ^ (ln & (CPR - 1));
             *reinterpret_cast<uint2*>(stage + ln * (D * 2) + chunk * 16 + hh * 8) = st;
         }
+    wave_lds_fence();
     const int cl = lane % CPR;
 #pragma unroll
     for (int i = 0; i < CPR / 2; ++i) {
@@ -915,6 +916,7 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             const int chunk = (4 * db + r) ^ (ln & (CPR - 1));
             *reinterpret_cast<uint2*>(stage + ln * (D * 2) + chunk * 16 + hh * 8) = st;
         }
+    wave_lds_fence();
     const int cl = lane % CPR;
 #pragma unroll
     for (int i = 0; i < CPR / 2; ++i) {

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
 OK, NULL, SHAPE, HEADS, HEADDIM, MASK, SCALE, PAGE, ALIGN, NOMEM, HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
-FULL, SEQ = -11, -12
+FULL, SEQ, CAPTURE = -11, -12, -13
 
 
 def _declared():
@@ -46,7 +46,7 @@ def test_header_declares_the_boundary():
     assert _codes() == {"ATTN_OK": OK, "ATTN_ERR_NULL": NULL, "ATTN_ERR_SHAPE": SHAPE, "ATTN_ERR_HEADS": HEADS,
                         "ATTN_ERR_HEADDIM": HEADDIM, "ATTN_ERR_MASK": MASK, "ATTN_ERR_SCALE": SCALE,
                         "ATTN_ERR_PAGE": PAGE, "ATTN_ERR_ALIGN": ALIGN, "ATTN_ERR_NOMEM": NOMEM, "ATTN_ERR_HIP": HIP,
-                        "ATTN_ERR_FULL": FULL, "ATTN_ERR_SEQ": SEQ}
+                        "ATTN_ERR_FULL": FULL, "ATTN_ERR_SEQ": SEQ, "ATTN_ERR_CAPTURE": CAPTURE}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -114,7 +114,8 @@ def _dec(lib, q=A, kp=A, vp=A, pt=A, sl=A, o=A, B=2, Hq=8, Hkv=2, D=128, ps=16, 
 @pytest.mark.parametrize("kwargs,code", [
     (dict(q=None), NULL), (dict(kp=None), NULL), (dict(vp=None), NULL), (dict(pt=None), NULL),
     (dict(sl=None), NULL), (dict(o=None), NULL),
-    (dict(B=-1), SHAPE), (dict(B=70000), SHAPE),
+    (dict(B=-1), SHAPE), (dict(B=70000), SHAPE), (dict(Hq=70000, Hkv=1), SHAPE),
+    (dict(B=65535, Hq=512, Hkv=8), SHAPE),   # B * Hq > 2^24
     (dict(Hq=0), HEADS), (dict(Hkv=0), HEADS), (dict(Hq=8, Hkv=3), HEADS),
     (dict(D=32), HEADDIM),
     (dict(ps=0), PAGE), (dict(ps=4), PAGE), (dict(ps=12), PAGE), (dict(ps=512), PAGE), (dict(ps=-16), PAGE),

@@ -100,3 +100,33 @@ def test_append_leaves_other_slots_untouched():
         page = int(d["page_table"][first + (n - 1) // 16])
         assert torch.all(kp[page, :, (n - 1) % 16] == 1)
         first += c
+
+
+def test_zero_length_sequence_writes_nothing():
+    # seq_lens[b] = 0 is outside the precondition (>= 1); the kernel must still
+    # leave every slot alone for it rather than write through the table entry
+    # before its own (the previous sequence's last page)
+    say("kv_append with a zero-length sequence")
+    Hkv, D, ps = 2, 128, 16
+    lens = torch.tensor([5, 0, 16, 0], dtype=torch.int32)
+    pages = [(int(n) + ps - 1) // ps for n in lens]
+    npages = sum(pages)
+    table = torch.randperm(npages, generator=torch.Generator().manual_seed(3)).to(torch.int32)
+    g = torch.Generator().manual_seed(4)
+    k_pool = torch.randn((npages, Hkv, ps, D), generator=g).to(torch.bfloat16)
+    v_pool = torch.randn((npages, Hkv, ps, D), generator=g).to(torch.bfloat16)
+    kn = torch.randn((4, Hkv, D), generator=g).to(torch.bfloat16)
+    vn = torch.randn((4, Hkv, D), generator=g).to(torch.bfloat16)
+    kp, vp, pt, sl, kn_d, vn_d = cuda(k_pool, v_pool, table, lens, kn, vn)
+    attn.kv_append(kn_d, vn_d, kp, vp, pt, sl)
+    torch.cuda.synchronize()
+    want_k, want_v = k_pool.clone(), v_pool.clone()
+    first = 0
+    for b, n in enumerate(lens.tolist()):
+        if n > 0:
+            page = int(table[first + (n - 1) // ps])
+            want_k[page, :, (n - 1) % ps] = kn[b]
+            want_v[page, :, (n - 1) % ps] = vn[b]
+        first += pages[b]
+    assert torch.equal(kp.cpu().view(torch.int16), want_k.view(torch.int16))
+    assert torch.equal(vp.cpu().view(torch.int16), want_v.view(torch.int16))

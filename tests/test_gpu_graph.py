@@ -67,3 +67,50 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for n, t in outs.items():
             assert torch.equal(t, eager[n]), f"replay {rep}: {n} differs from the eager result"
+
+
+def test_workspace_under_capture():
+    # a graph that captured a decode keeps its workspace after an eager call
+    # grows (replaces) the stream's buffer, and a capture that would need a
+    # larger workspace is refused instead of allocating
+    say("graph capture: workspace retired by growth, growth refused while capturing")
+    Hq, Hkv, D = 8, 2, 128
+    small = inputs.decode_inputs(4, Hq, Hkv, D, 16, 50, 400, "bf16", seed=81)
+    large = inputs.decode_inputs(64, Hq, Hkv, D, 16, 50, 400, "bf16", seed=82)
+    names = ("q", "k_pool", "v_pool", "page_table", "seq_lens")
+    sd = [small[n].cuda() for n in names]
+    ld = [large[n].cuda() for n in names]
+    o_small = torch.empty_like(sd[0])
+    o_large = torch.empty_like(ld[0])
+    s = torch.cuda.Stream()          # a stream of its own: a fresh workspace
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        attn.decode_paged(*sd, o=o_small)
+    s.synchronize()
+    want_small = o_small.clone()
+
+    g = torch.cuda.CUDAGraph()
+    refused = None
+    with torch.cuda.graph(g, stream=s):
+        attn.decode_paged(*sd, o=o_small)
+        try:
+            attn.decode_paged(*ld, o=o_large)   # needs a larger workspace
+        except RuntimeError as e:
+            refused = str(e)
+    torch.cuda.synchronize()
+    assert refused is not None and "captured" in refused, refused
+
+    with torch.cuda.stream(s):
+        attn.decode_paged(*ld, o=o_large)    # eager: grows the workspace
+    s.synchronize()
+    want_large = o_large.clone()
+    for _ in range(2):
+        o_small.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()                           # still the retired buffer
+        torch.cuda.synchronize()
+        assert torch.equal(o_small, want_small)
+    with torch.cuda.stream(s):
+        attn.decode_paged(*ld, o=o_large)
+    s.synchronize()
+    assert torch.equal(o_large, want_large)
