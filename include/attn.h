@@ -69,8 +69,11 @@ enum {
     ATTN_ERR_HIP = -10,     /* a HIP runtime call or kernel launch failed */
     ATTN_ERR_FULL = -11,    /* the page pool has too few free pages */
     ATTN_ERR_SEQ = -12,     /* a sequence id the page pool does not hold */
-    ATTN_ERR_CAPTURE = -13  /* the decode/backward workspace would have to grow
+    ATTN_ERR_CAPTURE = -13, /* the decode/backward workspace would have to grow
                                while `stream` is being captured into a graph */
+    ATTN_ERR_SCRATCH = -14  /* attn_decode_paged_noalloc: the call needs more
+                               than its fixed scratch (B * Hq * (D + 2) * 4 bytes
+                               > 16 MiB) */
 };
 
 /*
@@ -191,6 +194,32 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                       const int32_t* page_table, const int32_t* seq_lens,
                       int B, int Hq, int Hkv, int D, int page_size,
                       float scale, void* o, hipStream_t stream);
+
+/*
+ * attn_decode_paged_noalloc — attn_decode_paged that allocates nothing, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments,
+ * layouts, preconditions and result as attn_decode_paged (the same kernels).
+ *   The split-context partials go to a fixed scratch array of 16 MiB in
+ *   device memory instead of the library's workspace; each GPU the library
+ *   runs on holds its own copy from the first call on that device until the
+ *   process ends. The call makes no hipMalloc or hipFree and no other
+ *   allocating call; the array's address is looked up once per device on the
+ *   first call there, with that device current.
+ *   Limit: B * Hq * (D + 2) * 4 bytes must fit the 16 MiB (one context split
+ *   per (sequence, query head); B * Hq <= 32263 at D = 128), else
+ *   ATTN_ERR_SCRATCH with nothing enqueued. Beyond one split the call takes
+ *   as many splits as attn_decode_paged would, up to what the scratch holds.
+ *   Every call on one GPU shares that GPU's array and leaves its partials in
+ *   it: calls that overlap on one GPU (several streams, or several host
+ *   threads) race and give undefined results; serialise them.
+ *   Errors: those of attn_decode_paged (CAPTURE and NOMEM cannot occur), and
+ *   SCRATCH.
+ */
+int attn_decode_paged_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* page_table, const int32_t* seq_lens,
+                              int B, int Hq, int Hkv, int D, int page_size,
+                              float scale, void* o, hipStream_t stream);
 
 /*
  * attn_decode_paged_window — the same decode step restricted to a sliding

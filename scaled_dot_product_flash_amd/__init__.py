@@ -49,6 +49,8 @@ def load_library():
         fn.restype = i32
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp]
     lib.attn_decode_paged.restype = i32
+    lib.attn_decode_paged_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp]
+    lib.attn_decode_paged_noalloc.restype = i32
     lib.attn_decode_paged_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp]
     lib.attn_decode_paged_window.restype = i32
     lib.attn_fwd_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
@@ -249,6 +251,23 @@ def decode_paged(q, k_pool, v_pool, page_table, seq_lens, scale=None, o=None):
         rc = lib.attn_decode_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(),
                                    seq_lens.data_ptr(), B, Hq, Hkv, D, ps, scale, o.data_ptr(), _stream(q))
     _check(rc, "attn_decode_paged")
+    return o
+
+
+def decode_paged_noalloc(q, k_pool, v_pool, page_table, seq_lens, scale=None, o=None):
+    """decode_paged through attn_decode_paged_noalloc: the library allocates
+    nothing (its partials go to a fixed per-device scratch array; calls that
+    overlap on one GPU race). ``o`` should be passed by callers that must not
+    allocate either."""
+    import torch
+
+    lib = load_library()
+    B, Hq, Hkv, D, ps, scale, o = _decode_args(q, k_pool, v_pool, page_table, seq_lens, scale, o)
+    with torch.cuda.device(q.device):
+        rc = lib.attn_decode_paged_noalloc(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                           page_table.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, ps, scale,
+                                           o.data_ptr(), _stream(q))
+    _check(rc, "attn_decode_paged_noalloc")
     return o
 
 

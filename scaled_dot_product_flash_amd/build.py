@@ -18,8 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 
-SOURCES = ["api.cpp", "pages.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_paged.hip", "kv_append.hip",
-           "backward.hip"]
+SOURCES = ["api.cpp", "pages.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_paged.hip", "decode_noalloc.hip",
+           "kv_append.hip", "backward.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-mcode-object-version=5",

@@ -6,6 +6,7 @@
 #include "launch.h"
 
 #include <cmath>
+#include <algorithm>
 #include <cstdint>
 #include <map>
 #include <mutex>
@@ -118,9 +119,9 @@ int prefill_call(bool f32, const void* q, const void* k, const void* v, void* o,
     return hip_status(f32 ? attn::launch_prefill_f32(a, stream) : attn::launch_prefill_bf16(a, stream));
 }
 
-int decode_call(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
-                const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int page_size, float scale, int window,
-                void* o, hipStream_t stream) {
+int decode_validate(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                    const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int page_size, float scale, int window,
+                    const void* o) {
     if (B < 0) return ATTN_ERR_SHAPE;
     if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_HEADS;
     if (D != 64 && D != 128) return ATTN_ERR_HEADDIM;
@@ -135,11 +136,18 @@ int decode_call(const void* q, const void* k_pool, const void* v_pool, const int
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o) || !aligned4(page_table) ||
         !aligned4(seq_lens))
         return ATTN_ERR_ALIGN;
+    return ATTN_OK;
+}
 
+int decode_call(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int page_size, float scale, int window,
+                void* o, hipStream_t stream) {
+    int rc = decode_validate(q, k_pool, v_pool, page_table, seq_lens, B, Hq, Hkv, D, page_size, scale, window, o);
+    if (rc != ATTN_OK || B == 0) return rc;
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return ATTN_ERR_HIP;
     int ncu = 0;
-    int rc = cu_count(device, &ncu);
+    rc = cu_count(device, &ncu);
     if (rc != ATTN_OK) return rc;
     const bool mfma = attn::decode_on_mfma(B, Hq, Hkv, D, ncu);
     const int nsplit = attn::decode_nsplit(B, Hq, Hkv, ncu, mfma);
@@ -214,6 +222,29 @@ int attn_decode_paged_window(const void* q, const void* k_pool, const void* v_po
                              int window, void* o, hipStream_t stream) {
     return decode_call(q, k_pool, v_pool, page_table, seq_lens, B, Hq, Hkv, D, page_size, scale, window, o,
                        stream);
+}
+
+int attn_decode_paged_noalloc(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                              const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int page_size, float scale,
+                              void* o, hipStream_t stream) {
+    int rc = decode_validate(q, k_pool, v_pool, page_table, seq_lens, B, Hq, Hkv, D, page_size, scale, 0, o);
+    if (rc != ATTN_OK || B == 0) return rc;
+    // one split per (sequence, query head) at least must fit the scratch
+    const size_t per_split = (size_t)B * Hq * (size_t)(D + 2);
+    if (per_split > attn::kNoallocScratchFloats) return ATTN_ERR_SCRATCH;
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return ATTN_ERR_HIP;
+    float* ws = nullptr;
+    int ncu = 0;
+    if (attn::noalloc_scratch(device, &ws, &ncu) != hipSuccess) return ATTN_ERR_HIP;
+    const bool mfma = attn::decode_on_mfma(B, Hq, Hkv, D, ncu);
+    int nsplit = attn::decode_nsplit(B, Hq, Hkv, ncu, mfma);
+    // as many splits as the scratch holds (usually all the plain call takes)
+    const int fit = (int)std::min<size_t>(64, attn::kNoallocScratchFloats / per_split);
+    if (nsplit > fit) nsplit = fit;
+    attn::DecodeArgs a{q, k_pool, v_pool, page_table, seq_lens, o, B, Hq, Hkv, D, page_size, scale, 0,
+                       nsplit, ws, mfma};
+    return hip_status(attn::launch_decode_paged(a, stream));
 }
 
 int attn_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool, const int32_t* page_table,
@@ -292,6 +323,7 @@ const char* attn_strerror(int status) {
         case ATTN_ERR_FULL: return "the page pool has too few free pages";
         case ATTN_ERR_SEQ: return "the page pool holds no sequence with this id";
         case ATTN_ERR_CAPTURE: return "the workspace would have to grow while the stream is being captured";
+        case ATTN_ERR_SCRATCH: return "the call needs more than the 16 MiB of scratch the allocation-free decode holds (B * Hq * (D + 2) * 4 bytes)";
         default: return "unknown attn status code";
     }
 }

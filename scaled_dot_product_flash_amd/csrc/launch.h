@@ -90,6 +90,12 @@ bool decode_on_mfma(int B, int Hq, int Hkv, int D, int num_cu);
 int decode_nsplit(int B, int Hq, int Hkv, int num_cu, bool mfma);
 size_t decode_workspace_floats(int B, int Hq, int D, int nsplit);
 hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream);
+
+// Allocation-free decode: a fixed 16 MiB device array per device holds the
+// split partials. noalloc_scratch() returns its address on `device` (which
+// must be current; looked up once per device) and the device's CU count.
+constexpr size_t kNoallocScratchFloats = (size_t)4 << 20;
+hipError_t noalloc_scratch(int device, float** ptr, int* num_cu);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 int backward_kv_splits(int B, int Hkv, int Sq, int Sk, int num_cu);
 size_t backward_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, int kv_splits);

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
 OK, NULL, SHAPE, HEADS, HEADDIM, MASK, SCALE, PAGE, ALIGN, NOMEM, HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
-FULL, SEQ, CAPTURE = -11, -12, -13
+FULL, SEQ, CAPTURE, SCRATCH = -11, -12, -13, -14
 
 
 def _declared():
@@ -40,13 +40,14 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared() == ["attn_bwd", "attn_decode_paged", "attn_decode_paged_window", "attn_fwd", "attn_fwd_f32",
+    assert _declared() == ["attn_bwd", "attn_decode_paged", "attn_decode_paged_noalloc", "attn_decode_paged_window", "attn_fwd", "attn_fwd_f32",
                            "attn_fwd_f32_lse", "attn_fwd_lse", "attn_fwd_paged", "attn_kv_append", "attn_pages_create", "attn_pages_destroy", "attn_pages_free_count",
                            "attn_pages_resize", "attn_pages_table", "attn_release", "attn_strerror"]
     assert _codes() == {"ATTN_OK": OK, "ATTN_ERR_NULL": NULL, "ATTN_ERR_SHAPE": SHAPE, "ATTN_ERR_HEADS": HEADS,
                         "ATTN_ERR_HEADDIM": HEADDIM, "ATTN_ERR_MASK": MASK, "ATTN_ERR_SCALE": SCALE,
                         "ATTN_ERR_PAGE": PAGE, "ATTN_ERR_ALIGN": ALIGN, "ATTN_ERR_NOMEM": NOMEM, "ATTN_ERR_HIP": HIP,
-                        "ATTN_ERR_FULL": FULL, "ATTN_ERR_SEQ": SEQ, "ATTN_ERR_CAPTURE": CAPTURE}
+                        "ATTN_ERR_FULL": FULL, "ATTN_ERR_SEQ": SEQ, "ATTN_ERR_CAPTURE": CAPTURE,
+                        "ATTN_ERR_SCRATCH": SCRATCH}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -105,7 +106,10 @@ def test_prefill_empty_calls_are_no_ops(lib, f32):
     assert _fwd(lib, q=None, k=None, v=None, o=None, Sq=0, causal=0, f32=f32) == OK
 
 
-def _dec(lib, q=A, kp=A, vp=A, pt=A, sl=A, o=A, B=2, Hq=8, Hkv=2, D=128, ps=16, scale=0.1, window=None):
+def _dec(lib, q=A, kp=A, vp=A, pt=A, sl=A, o=A, B=2, Hq=8, Hkv=2, D=128, ps=16, scale=0.1, window=None,
+         noalloc=False):
+    if noalloc:
+        return lib.attn_decode_paged_noalloc(q, kp, vp, pt, sl, B, Hq, Hkv, D, ps, scale, o, None)
     if window is None:
         return lib.attn_decode_paged(q, kp, vp, pt, sl, B, Hq, Hkv, D, ps, scale, o, None)
     return lib.attn_decode_paged_window(q, kp, vp, pt, sl, B, Hq, Hkv, D, ps, scale, window, o, None)
@@ -125,8 +129,24 @@ def _dec(lib, q=A, kp=A, vp=A, pt=A, sl=A, o=A, B=2, Hq=8, Hkv=2, D=128, ps=16, 
 ])
 def test_decode_validation(lib, kwargs, code):
     assert _dec(lib, **kwargs) == code
-    # the windowed entry point validates the same arguments the same way
+    # the windowed and the allocation-free entry points validate the same
+    # arguments the same way
     assert _dec(lib, window=5, **kwargs) == code
+    assert _dec(lib, noalloc=True, **kwargs) == code
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D", [(32264, 1, 1, 128), (1000, 33, 1, 128), (64, 1024, 8, 128),
+                                        (16384, 4, 4, 64)])
+def test_decode_noalloc_scratch_limit(lib, B, Hq, Hkv, D):
+    # B * Hq * (D + 2) * 4 bytes above the 16 MiB scratch: refused before any
+    # HIP call; one fewer (sequence, head) unit than the limit passes that check
+    assert B * Hq * (D + 2) * 4 > 16 << 20
+    assert _dec(lib, B=B, Hq=Hq, Hkv=Hkv, D=D, noalloc=True) == SCRATCH
+    assert _dec(lib, B=B, Hq=Hq, Hkv=Hkv, D=D, noalloc=True, q=None) == NULL  # validated first
+
+
+def test_decode_noalloc_empty_batch_is_a_no_op(lib):
+    assert _dec(lib, q=None, kp=None, vp=None, pt=None, sl=None, o=None, B=0, noalloc=True) == OK
 
 
 @pytest.mark.parametrize("window", [-1, -100])
