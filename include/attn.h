@@ -54,9 +54,9 @@ enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = -1,     /* a required pointer is NULL */
     ATTN_ERR_SHAPE = -2,    /* a size is negative or zero where it must be >= 1,
-                               causal with Sq > Sk, an element count overflows
-                               64-bit addressing, or one (batch, kv head) slice
-                               of K/V exceeds 2^31 bytes in float32
+                               causal with Sq > Sk, Sq > 2^30, an element count
+                               overflows 64-bit addressing, or one (batch, kv
+                               head) slice of K/V exceeds 2^31 bytes in float32
                                (Sk * D * 4 >= 2^31) */
     ATTN_ERR_HEADS = -3,    /* Hq < 1, Hkv < 1 or Hq % Hkv != 0 */
     ATTN_ERR_HEADDIM = -4,  /* D is not 64 or 128 */

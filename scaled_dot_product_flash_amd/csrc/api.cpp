@@ -15,6 +15,20 @@
 
 namespace {
 
+// largest Sq (query rows per head) any call accepts
+constexpr int kMaxRows = 1 << 30;
+
+// A dispatch holds at most 2^32 work-items per dimension. The bf16 prefill
+// kernels launch one workgroup per 128 (256 threads) or 256 (512 threads)
+// query rows, the float32 one per 16 rows (256 threads), up to twice as many
+// after the XCD deal rounds the grid up: at most 2^31 work-items below these
+// limits.
+bool prefill_grid_fits(int B, int Hq, int Sq, bool f32) {
+    const long long rows_per_tile = f32 ? 16 : 128;
+    const long long tiles = (long long)B * Hq * (((long long)Sq + rows_per_tile - 1) / rows_per_tile);
+    return tiles <= (f32 ? (1LL << 23) : (1LL << 22));
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
@@ -25,7 +39,7 @@ bool product_fits(long long a, long long b, long long c, long long d) {
 }
 
 int validate_prefill(const void* q, const void* k, const void* v, const void* o, int B, int Hq, int Hkv,
-                     int Sq, int Sk, int D, float scale, int causal, int window, bool* empty) {
+                     int Sq, int Sk, int D, float scale, int causal, int window, bool f32, bool* empty) {
     *empty = false;
     if (B < 0 || Sq < 0) return ATTN_ERR_SHAPE;
     if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_HEADS;
@@ -39,12 +53,13 @@ int validate_prefill(const void* q, const void* k, const void* v, const void* o,
     }
     if (Sk < 1) return ATTN_ERR_SHAPE;
     if (causal && Sq > Sk) return ATTN_ERR_SHAPE;
+    // row counts stay far from int overflow in the launchers' tile arithmetic
+    if (Sq > kMaxRows) return ATTN_ERR_SHAPE;
     if (!product_fits(B, Hq, Sq, D) || !product_fits(B, Hkv, Sk, D)) return ATTN_ERR_SHAPE;
     // one (batch, kv head) slice of K or V is addressed with 32-bit byte offsets
     if ((long long)Sk * D * 4 > 0x7FFFFFFFLL) return ATTN_ERR_SHAPE;
     // grid of either kernel (at most one workgroup per 64 rows, rounded to 8)
-    const long long items = (long long)B * Hq * ((Sq + 63) / 64) + 8;
-    if (items > 0x7FFFFFFFLL) return ATTN_ERR_SHAPE;
+    if (!prefill_grid_fits(B, Hq, Sq, f32)) return ATTN_ERR_SHAPE;
     if (!q || !k || !v || !o) return ATTN_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
     return ATTN_OK;
@@ -107,7 +122,7 @@ int prefill_call(bool f32, const void* q, const void* k, const void* v, void* o,
                  int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale, int causal, int window,
                  hipStream_t stream) {
     bool empty = false;
-    const int rc = validate_prefill(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, &empty);
+    const int rc = validate_prefill(q, k, v, o, B, Hq, Hkv, Sq, Sk, D, scale, causal, window, f32, &empty);
     if (rc != ATTN_OK || empty) return rc;
     if (want_lse && !lse) return ATTN_ERR_NULL;
     if (want_lse && !aligned4(lse)) return ATTN_ERR_ALIGN;
@@ -195,9 +210,8 @@ int attn_fwd_paged(const void* q, const void* k_pool, const void* v_pool, const 
     if (window < 0 || (window > 0 && !causal)) return ATTN_ERR_MASK;
     if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
     if (B == 0 || Sq == 0) return ATTN_OK;
-    if (!product_fits(B, Hq, Sq, D)) return ATTN_ERR_SHAPE;
-    const long long items = (long long)B * Hq * ((Sq + 63) / 64) + 8;
-    if (items > 0x7FFFFFFFLL) return ATTN_ERR_SHAPE;
+    if (Sq > kMaxRows || !product_fits(B, Hq, Sq, D)) return ATTN_ERR_SHAPE;
+    if (!prefill_grid_fits(B, Hq, Sq, false)) return ATTN_ERR_SHAPE;
     if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !o) return ATTN_ERR_NULL;
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o) || !aligned4(page_table) ||
         !aligned4(seq_lens) || (lse && !aligned4(lse)))
@@ -254,7 +268,8 @@ int attn_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_p
     if (D != 64 && D != 128) return ATTN_ERR_HEADDIM;
     if (page_size < 8 || page_size > 256 || (page_size & (page_size - 1)) != 0) return ATTN_ERR_PAGE;
     if (B == 0) return ATTN_OK;
-    if (B > 0x7FFFFFFF / 2) return ATTN_ERR_SHAPE;
+    // one workgroup of 128 threads per sequence
+    if (B > (1 << 24)) return ATTN_ERR_SHAPE;
     if (!k_new || !v_new || !k_pool || !v_pool || !page_table || !seq_lens) return ATTN_ERR_NULL;
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool) ||
         !aligned4(page_table) || !aligned4(seq_lens))
@@ -275,12 +290,18 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     if (B == 0 || (Sq == 0 && Sk == 0)) return ATTN_OK;
     if (Sk < 1) return ATTN_ERR_SHAPE;
     if (causal && Sq > Sk) return ATTN_ERR_SHAPE;
+    // row counts stay far from int overflow in the launchers' tile arithmetic
+    if (Sq > kMaxRows) return ATTN_ERR_SHAPE;
     if (!product_fits(B, Hq, Sq, D) || !product_fits(B, Hkv, Sk, D)) return ATTN_ERR_SHAPE;
     // one head's Q/dO or K/V rows (plus a tile of overrun) are addressed with
     // 32-bit byte offsets
     if ((long long)Sk * D * 4 > 0x7FFFFFFFLL || (long long)Sq * D * 4 > 0x7FFFFFFFLL) return ATTN_ERR_SHAPE;
-    const long long items = (long long)B * Hq * ((Sq + 127) / 128) + (long long)B * Hkv * ((Sk + 127) / 128) + 16;
-    if (items > 0x7FFFFFFFLL) return ATTN_ERR_SHAPE;
+    // grids: dQ one 256-thread workgroup per 128 query rows, dK/dV one
+    // 512-thread workgroup per 256 keys (up to 16 runs each when the blocks
+    // are few), both below 2^31 work-items within these limits
+    if ((long long)B * Hq * (((long long)Sq + 127) / 128) > (1LL << 22) ||
+        (long long)B * Hkv * (((long long)Sk + 255) / 256) > (1LL << 22))
+        return ATTN_ERR_SHAPE;
     // with no query rows only dk and dv (zeros) are written; the query-side
     // tensors are empty and their pointers may be NULL
     const bool rows = Sq > 0;

@@ -822,7 +822,7 @@ hipError_t launch_d(const BackwardArgs& a, hipStream_t stream) {
         const long long grid = deal.grid;
         // causal items: order by weight (two workgroups per CU)
         const int pair = balance_arg(nitems, deal.chunk, (long long)G * nqt, grid, a.causal, a.num_cu, 2);
-        if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+        if (!grid_fits(grid, kThreads)) return hipErrorInvalidValue;
         hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o,
                            (const uint16_t*)a.dout, a.lse, delta, l2, (uint16_t*)a.dq, qt, dot, a.Hq, a.Hkv, a.Sq, a.Sk,
@@ -836,7 +836,7 @@ hipError_t launch_d(const BackwardArgs& a, hipStream_t stream) {
     float* part = nsplit > 1 ? reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(dot) + align256(tbytes))
                              : nullptr;
     const long long grid = (long long)nbg * nkt * nsplit;
-    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    if (!grid_fits(grid, 64 * kKvWaves)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)grid), dim3(64 * kKvWaves), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                        qt, dot, l2, delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.Hq, a.Hkv, a.Sq, a.Sk, a.scale, c2,

@@ -21,6 +21,11 @@ __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// A dispatch holds the grid size in work-items, 32 bits per dimension.
+inline bool grid_fits(long long workgroups, int threads) {
+    return workgroups > 0 && workgroups * (long long)threads < (1LL << 32);
+}
+
 struct PrefillArgs {
     const void* q;
     const void* k;

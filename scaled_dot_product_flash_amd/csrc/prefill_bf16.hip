@@ -931,7 +931,7 @@ hipError_t launch_pipe(const PrefillArgs& a, hipStream_t stream) {
     const int nqt = (a.Sq + 32 * NW - 1) / (32 * NW);
     const long long nitems = (long long)a.B * a.Hq * nqt;
     const Deal deal = make_deal(nitems, (long long)(a.Hq / a.Hkv) * nqt, a.Hq / a.Hkv, PAGED);
-    if (deal.grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    if (!grid_fits(deal.grid, 64 * NW)) return hipErrorInvalidValue;
     float c2 = a.scale * 1.4426950408889634f;
     if (c2 == 0.f) c2 = 1e-30f;
     int ps_log2 = 0;
@@ -953,7 +953,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     const int nqt = (a.Sq + kBM - 1) / kBM;
     const long long nitems = (long long)a.B * a.Hq * nqt;
     const Deal deal = make_deal(nitems, (long long)(a.Hq / a.Hkv) * nqt, a.Hq / a.Hkv, PAGED);
-    if (deal.grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    if (!grid_fits(deal.grid, kThreads)) return hipErrorInvalidValue;
     // causal items: order by weight (three workgroups per CU)
     const int pair = PAGED ? 0
                            : balance_arg(nitems, deal.chunk, (long long)(a.Hq / a.Hkv) * nqt, deal.grid, a.causal,

@@ -175,7 +175,7 @@ template <int D>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     const int nqt = (a.Sq + kRows - 1) / kRows;
     const long long grid = (long long)a.B * a.Hq * nqt;
-    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    if (!grid_fits(grid, kThreads)) return hipErrorInvalidValue;
     const float c2 = a.scale * 1.4426950408889634f;
     hipLaunchKernelGGL((prefill_f32_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,

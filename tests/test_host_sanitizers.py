@@ -1,0 +1,79 @@
+"""The library's host code under the address and undefined-behaviour sanitizers.
+
+Every host source of libattn.so (the C ABI, the page pool and the launchers
+in the kernel files) is compiled for the host only with ASan and UBSan and
+linked against tests/native/hip_host_stub.cpp, a stand-in HIP runtime that
+plays one 256-CU device, allocates "device" memory on the host heap and
+checks every kernel launch against the hardware's grid limits instead of
+running it. tests/native/abi_host_check.cpp then drives each entry point:
+the documented error codes, a sweep over boundary values of every size and
+mask argument, and the page pool under random resizes. Any sanitizer report
+or launch-limit violation aborts the program. CPU only.
+"""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "scaled_dot_product_flash_amd", "csrc")
+NATIVE = os.path.join(ROOT, "tests", "native")
+SOURCES = ["api.cpp", "pages.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_paged.hip",
+           "decode_noalloc.hip", "kv_append.hip", "backward.hip"]
+# host-side sanitizer flags: each -fsanitize= sits right after -Xarch_host so
+# the device side of a hipcc line never gets it
+HOST_SAN = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=all"]
+GXX_SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+
+
+def _tool(name, fallback):
+    return shutil.which(name) or (fallback if os.path.exists(fallback) else None)
+
+
+@pytest.fixture(scope="module")
+def host_check(tmp_path_factory):
+    hipcc = _tool("hipcc", "/opt/rocm/bin/hipcc")
+    gxx = _tool("g++", "/usr/bin/g++")
+    if hipcc is None or gxx is None:
+        pytest.skip("hipcc and g++ are needed")
+    d = tmp_path_factory.mktemp("host_san")
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = str(d / (src + ".o"))
+        cmd = [hipcc, "-x", "hip", "--cuda-host-only", "--offload-arch=gfx950", "-O1", "-g", "-std=c++17",
+               "-fPIC", "-fno-omit-frame-pointer", *HOST_SAN, *inc, "-c", os.path.join(CSRC, src), "-o", obj]
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+        objs.append(obj)
+    for p, src in zip(procs, SOURCES):
+        out = p.communicate(timeout=600)[0]
+        assert p.returncode == 0, f"{src}: {out[-3000:]}"
+    # host-only objects reference their (absent) device images by name; give
+    # the stand-in runtime empty ones to register
+    nm = subprocess.run(["nm", "-u", *objs], capture_output=True, text=True, check=True).stdout
+    fatbins = sorted(set(re.findall(r"\b(__hip_fatbin_\w+)", nm)))
+    defs = d / "fatbins.c"
+    defs.write_text("".join(f"char {n}[64];\n" for n in fatbins))
+    exe = str(d / "abi_host_check")
+    for src in ("hip_host_stub.cpp", "abi_host_check.cpp"):
+        subprocess.run([gxx, "-O1", "-g", "-std=c++17", "-fno-omit-frame-pointer", *GXX_SAN, "-D__HIP_PLATFORM_AMD__",
+                        "-I", "/opt/rocm/include", *inc, "-c", os.path.join(NATIVE, src), "-o",
+                        str(d / (src + ".o"))], check=True, capture_output=True, text=True, timeout=300)
+    subprocess.run([gxx, "-c", str(defs), "-o", str(d / "fatbins.o")], check=True, timeout=60)
+    subprocess.run([gxx, *GXX_SAN, "-o", exe, *objs, str(d / "hip_host_stub.cpp.o"),
+                    str(d / "abi_host_check.cpp.o"), str(d / "fatbins.o")],
+                   check=True, capture_output=True, text=True, timeout=300)
+    return exe
+
+
+def test_host_code_under_sanitizers(host_check):
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    run = subprocess.run([host_check, "200000"], capture_output=True, text=True, timeout=600, env=env)
+    assert run.returncode == 0, (run.stdout[-3000:], run.stderr[-6000:])
+    assert run.stdout.strip().endswith("host checks ok")
+    launches = int(re.search(r"launches (\d+)", run.stdout).group(1))
+    assert launches > 50000    # the sweep reached the launchers, not only validation
