@@ -55,9 +55,12 @@ enum {
     ATTN_ERR_NULL = -1,     /* a required pointer is NULL */
     ATTN_ERR_SHAPE = -2,    /* a size is negative or zero where it must be >= 1,
                                causal with Sq > Sk, Sq > 2^30, an element count
-                               overflows 64-bit addressing, or one (batch, kv
+                               overflows 64-bit addressing, one (batch, kv
                                head) slice of K/V exceeds 2^31 bytes in float32
-                               (Sk * D * 4 >= 2^31) */
+                               (Sk * D * 4 >= 2^31), or the launch grid would
+                               exceed the dispatch limit: prefill B * Hq *
+                               ceil(Sq / 128) > 2^22 (bf16) or B * Hq *
+                               ceil(Sq / 16) > 2^23 (float32) */
     ATTN_ERR_HEADS = -3,    /* Hq < 1, Hkv < 1 or Hq % Hkv != 0 */
     ATTN_ERR_HEADDIM = -4,  /* D is not 64 or 128 */
     ATTN_ERR_MASK = -5,     /* causal not 0/1, window < 0, or (prefill) window > 0
@@ -255,7 +258,7 @@ int attn_decode_paged_window(const void* q, const void* k_pool, const void* v_po
  *   The page holding that position must already be in the table (see
  *   attn_pages_resize); the device-side preconditions of attn_decode_paged
  *   apply. Sequences must not share physical pages.
- *   Errors: NULL, SHAPE (B < 0), HEADS (Hkv < 1), HEADDIM, PAGE, ALIGN
+ *   Errors: NULL, SHAPE (B < 0 or B > 2^24), HEADS (Hkv < 1), HEADDIM, PAGE, ALIGN
  *   (16 bytes for tensors, 4 for the int32 arrays), HIP. B == 0 is a no-op.
  */
 int attn_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
@@ -327,8 +330,10 @@ int attn_pages_table(const attn_page_pool* pool, const int64_t* seq_ids, int n, 
  *   partial dk and dv of up to 16 runs per block (2 * runs * B * Hkv * Sk * D
  *   floats), summed in a fixed order: the result is bit-reproducible.
  *   Errors: those of attn_fwd for the same sizes, plus NULL / ALIGN for the
- *   extra pointers, NOMEM for the workspace, and SHAPE when Sq * D or Sk * D
- *   exceeds 2^29 (one head's rows are addressed with 32-bit offsets).
+ *   extra pointers, NOMEM and CAPTURE for the workspace, and SHAPE when
+ *   Sq * D or Sk * D exceeds 2^29 (one head's rows are addressed with 32-bit
+ *   offsets) or B * Hq * ceil(Sq / 128) or B * Hkv * ceil(Sk / 256) exceeds
+ *   2^22 (launch grids).
  *   B == 0 is a no-op; Sq == 0 writes zero dk and dv and then accepts NULL
  *   for q, k, v, o, dout, lse and dq.
  */

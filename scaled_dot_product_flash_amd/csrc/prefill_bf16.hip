@@ -681,6 +681,19 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         for (int v = 8 * half; v < 8 * half + 8; ++v) mx = NEG ? fminf(mx, sb[v]) : fmaxf(mx, sb[v]);
         return mx;
     };
+    // the extreme of 8 values and mx as a tree of depth 2 (three independent
+    // 3-way extremes, then one), pinned where it is called: without the pin
+    // the compiler sinks every extreme of the block to its end, where they
+    // form one dependent chain behind the block's last MFMA
+    auto ext8t = [&](const f32x16& sb, int half, float mx) __attribute__((always_inline)) {
+        const int v = 8 * half;
+        auto e3 = [&](float a, float b, float c) __attribute__((always_inline)) {
+            return NEG ? fminf(fminf(a, b), c) : fmaxf(fmaxf(a, b), c);
+        };
+        float r = e3(e3(sb[v], sb[v + 1], sb[v + 2]), e3(sb[v + 3], sb[v + 4], sb[v + 5]), e3(sb[v + 6], sb[v + 7], mx));
+        asm volatile("" : "+v"(r));
+        return r;
+    };
     // after the row extreme of a tile: lazy move of the reference maximum
     auto settle = [&](float mx) __attribute__((always_inline)) {
         const float2 hv = halves(mx);
@@ -778,8 +791,8 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                 }
             }
             if constexpr (NEXT) {
-                if (c == 6 || c == 7) mx = ext8(snew[1], c - 6, mx);
-                if (c == 9) mx = ext8(snew[0], 1, ext8(snew[0], 0, mx));
+                if (c == 6 || c == 7) mx = ext8t(snew[1], c - 6, mx);
+                if (c == 9) mx = ext8t(snew[0], 1, ext8t(snew[0], 0, mx));
             }
         }
         l_run = la + lb;
@@ -839,8 +852,8 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     // the group's first tiles compute those fully masked tiles, which add
     // exact zeros.
     f32x16 sA[KB], sB[KB];
-    issue(krs, t_begin, k_lds0, false);
-    // Q rows into registers, queued behind the first K tile's DMA
+    // Q rows into registers, then the first tiles K(t0), K(t0+1) and V(t0)
+    // (their buffers are all free), so the item waits for memory once
     {
         const bool ok = qrow < Sq;
         const uint16_t* qp = Q + qo_base + (size_t)(ok ? qrow : 0) * D + 8 * hh;
@@ -850,11 +863,12 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             qreg[st] = as_bf16x8(x);
         }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    issue(krs, t_begin, k_lds0, false);
     if (t_begin + 1 < t_end) issue(krs, t_begin + 1, k_lds1, false);
     issue(vrs, t_begin, v_lds0, true);
     if constexpr (PAGED) pid = page_ids(t_begin + 2, t_begin + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     {
 #pragma unroll
         for (int st = 0; st < DS; ++st)
