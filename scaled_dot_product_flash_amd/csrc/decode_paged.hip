@@ -46,6 +46,7 @@
 //    (m, l, o) into the bf16 output.
 
 #include "launch.h"
+#include "paging.h"
 
 #include <cmath>
 
@@ -164,7 +165,7 @@ void decode_split_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __rest
 
     // off_b = sum_{j<b} ceil(len_j / ps), the sequence's first page-table entry
     int part = 0;
-    for (int j = tid; j < b; j += kThreads) part += (lens[j] + ps - 1) >> ps_log2;
+    for (int j = tid; j < b; j += kThreads) part += seq_pages(lens[j], ps_log2);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
     if (lane == 0) sh_red[wave] = part;
@@ -173,12 +174,10 @@ void decode_split_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __rest
     const int len = lens[b];
     const int32_t* tab = table + off_b;
 
-    // visible tokens first .. len-1; blocks blk0 .. blk0 + nblk - 1
-    const int first = window > 0 ? max(0, len - window) : 0;
-    const int blk0 = first / TB;
-    const int nblk = (len + TB - 1) / TB - blk0;
-    const int blk_begin = blk0 + (int)((long long)nblk * split / nsplit);
-    const int blk_end = blk0 + (int)((long long)nblk * (split + 1) / nsplit);
+    // visible tokens first .. len-1; this split's blocks [blk_begin, blk_end)
+    const int first = window_first(len, window);
+    const UnitRun run = split_units(first, len, TB, split, nsplit);
+    const int blk_begin = run.begin, blk_end = run.end;
 
     // q of the packed heads: 8 dims (4 bf16 pairs) per lane and head
     uint32_t qv[GH][4];
@@ -197,9 +196,6 @@ void decode_split_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __rest
         for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
     }
 
-    const size_t head_stride = (size_t)ps * D;            // one (page, head) tile
-    const size_t page_stride = (size_t)Hkv * head_stride;
-
     // K/V pages are streamed once per decode step: nontemporal loads keep them
     // from displacing other data in the caches. The page base is wave-uniform
     // (scalar), the lane's offset inside the (page, head) tile is 32-bit.
@@ -210,8 +206,7 @@ void decode_split_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __rest
             const int t0 = blk * TB + i * TPI;           // first token of this load
             if (t0 < len) {
                 const int page = __builtin_amdgcn_readfirstlane(tab[t0 >> ps_log2]);
-                const size_t tile = (size_t)page * page_stride + (size_t)g * head_stride +
-                                    (size_t)(t0 & (ps - 1)) * D;
+                const size_t tile = pool_tile(page, g, Hkv, ps_log2, D) + (size_t)(t0 & (ps - 1)) * D;
                 kx[i] = ld16_nt(Kp + tile + lane_off);
                 vx[i] = ld16_nt(Vp + tile + lane_off);
             } else {
@@ -439,7 +434,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer resource word 3, gfx9 family
 constexpr int kTT = 32;                  // tokens per tile
-constexpr int kStages = 2;               // tiles per wave: one in use, one in flight (V stages below)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -456,7 +450,6 @@ void decode_mfma_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __restr
     constexpr int RPS = 64 / CPR;       // rows per 1 KiB DMA slot
     constexpr int VT = kTT * D * 2;     // bytes of a V tile
     constexpr int VSLOTS = VT / 1024;
-    constexpr int OPS = DS + VSLOTS;    // vector memory instructions per tile
     // one LDS object per stage (four waves' tiles each), so that the
     // compiler's wait for DMA into LDS can tell the stages apart
     __shared__ __attribute__((aligned(16))) unsigned char vl0[kWaves * VT];
@@ -505,7 +498,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __restr
 
     // off_b = sum_{j<b} ceil(len_j / ps), the sequence's first page-table entry
     int part = 0;
-    for (int j = tid; j < b; j += kThreads) part += (lens[j] + ps - 1) >> ps_log2;
+    for (int j = tid; j < b; j += kThreads) part += seq_pages(lens[j], ps_log2);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
     if (lane == 0) sh_red[wave] = part;
@@ -533,11 +526,9 @@ void decode_mfma_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __restr
 
     // this split's tiles of the visible tokens first .. len-1; wave w takes
     // tiles tbeg + w, tbeg + w + 4, ...
-    const int first = window > 0 ? max(0, len - window) : 0;
-    const int tl0 = first / kTT;
-    const int ntile = (len + kTT - 1) / kTT - tl0;
-    const int tbeg = tl0 + (int)((long long)ntile * split / nsplit);
-    const int tend = tl0 + (int)((long long)ntile * (split + 1) / nsplit);
+    const int first = window_first(len, window);
+    const UnitRun run = split_units(first, len, kTT, split, nsplit);
+    const int tbeg = run.begin, tend = run.end;
     const int nmine = tend - tbeg > wave ? (tend - tbeg - wave + kWaves - 1) / kWaves : 0;
 
     // Q^T operand: column ln = head hg0 + ln, k-chunk = dims 16 s + 8 hh .. +7
@@ -549,8 +540,6 @@ void decode_mfma_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __restr
         for (int s = 0; s < DS; ++s) qreg[s] = as_bf16x8(ok ? ld16(qp + 16 * s) : make_uint4(0, 0, 0, 0));
     }
 
-    const size_t head_stride = (size_t)ps * D;          // one (page, kv head) tile
-    const size_t page_stride = (size_t)Hkv * head_stride;
     auto vswz = [](int row) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); };
     unsigned char* const vs0 = vl0 + wave * VT;       // this wave's V stages
     unsigned char* const vs1 = vl1 + wave * VT;
@@ -572,8 +561,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __restr
         const int tok = dummy ? len - 1 : min(j0 + ln, len - 1);
         const int page = dummy ? __builtin_amdgcn_readfirstlane(tab[last_page])
                                : pick(min(max((tok >> ps_log2) - p0, 0), 3));
-        const uint16_t* kp = Kp + (size_t)page * page_stride + (size_t)g * head_stride +
-                             (size_t)(tok & (ps - 1)) * D + 8 * hh;
+        const uint16_t* kp = Kp + pool_tile(page, g, Hkv, ps_log2, D) + (size_t)(tok & (ps - 1)) * D + 8 * hh;
 #pragma unroll
         for (int s = 0; s < DS; ++s) kdst[s] = ld16_nt(kp + 16 * s);
         // V: slot sl holds rows sl * RPS .. +RPS-1, all in one page
@@ -582,7 +570,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ Qp, const uint16_t* __restr
             const int r0 = j0 + sl * RPS;
             const bool any = !dummy && r0 < len;
             const int vpage = pick(min(max((r0 >> ps_log2) - p0, 0), 3));
-            const uint16_t* tile = Vp + (size_t)vpage * page_stride + (size_t)g * head_stride;
+            const uint16_t* tile = Vp + pool_tile(vpage, g, Hkv, ps_log2, D);
             const __amdgpu_buffer_rsrc_t rs =
                 __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, any ? ps * D * 2 : 0, kRsrcWord3);
             const int row = sl * RPS + lane / CPR;

@@ -15,6 +15,7 @@
 // a few KiB per sequence, so the kernel is bound by launch latency, not HBM.
 
 #include "launch.h"
+#include "paging.h"
 
 namespace attn {
 namespace {
@@ -32,7 +33,7 @@ void kv_append_kernel(const uint16_t* __restrict__ k_new, const uint16_t* __rest
     const int ps = 1 << ps_log2;
 
     int part = 0;
-    for (int j = tid; j < b; j += kThreads) part += (lens[j] + ps - 1) >> ps_log2;
+    for (int j = tid; j < b; j += kThreads) part += seq_pages(lens[j], ps_log2);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
     if ((tid & 63) == 0) sh_part[tid >> 6] = part;
@@ -47,7 +48,7 @@ void kv_append_kernel(const uint16_t* __restrict__ k_new, const uint16_t* __rest
     // own (another sequence's last page)
     if (t < 0) return;
     const int page = table[off_b + (t >> ps_log2)];
-    const size_t dst = (((size_t)page * Hkv) * ps + (size_t)(t & (ps - 1))) * D;  // head 0 of the slot
+    const size_t dst = pool_tile(page, 0, Hkv, ps_log2, D) + (size_t)(t & (ps - 1)) * D;  // head 0 of the slot
     const size_t head_stride = (size_t)ps * D;
     const int chunks = D / 8;                      // 16-byte chunks per head row
     for (int i = tid; i < Hkv * chunks; i += kThreads) {

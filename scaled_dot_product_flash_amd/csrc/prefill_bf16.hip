@@ -44,6 +44,7 @@
 
 #include "launch.h"
 #include "deal.h"
+#include "paging.h"
 
 #include <algorithm>
 #include <cmath>
@@ -144,7 +145,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         }
         __shared__ int sh_part[kWaves];
         int part = 0;
-        for (int j = tid; j < b; j += kThreads) part += (lens[j] + (1 << ps_log2) - 1) >> ps_log2;
+        for (int j = tid; j < b; j += kThreads) part += seq_pages(lens[j], ps_log2);
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
         if (lane == 0) sh_part[wave] = part;
@@ -222,7 +223,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                 const int r0 = j0 + sl * (64 / CPR);
                 const bool any = r0 < Sk;
                 const int page = any ? table[off_b + (r0 >> ps_log2)] : 0;
-                const size_t tb = ((size_t)page * Hkv + g) * ((size_t)ps * D);
+                const size_t tb = pool_tile(page, g, Hkv, ps_log2, D);
                 const int bytes = any ? ps * D * 2 : 0;
                 const __amdgpu_buffer_rsrc_t pk = __builtin_amdgcn_make_buffer_rsrc((void*)(K + tb), 0, bytes, kRsrcWord3);
                 const __amdgpu_buffer_rsrc_t pv = __builtin_amdgcn_make_buffer_rsrc((void*)(V + tb), 0, bytes, kRsrcWord3);
@@ -293,22 +294,37 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         const float masked = NEG ? INFINITY : -INFINITY;
         if (edge) {
             asm volatile("");
+            // key j0 + base + c is visible iff c <= lim_hi and c > lim_lo, with
+            // c the value's compile-time column in the tile: one compare per
+            // bound and value
+            const int base = j0 + 4 * hh;
+            const int sk_hi = Sk - 1 - base;
+            const int lim_hi = causal ? min(qpos - base, sk_hi) : sk_hi;
+            const int lim_lo = window > 0 ? qpos - window - base : -1;
 #pragma unroll
             for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int j = j0 + 32 * kbk + 8 * (v >> 2) + 4 * hh + (v & 3);
-                    bool ok = j < Sk;
-                    if (causal) ok = ok && j <= qpos;
-                    if (window > 0) ok = ok && j > qpos - window;
+                    const int c = 32 * kbk + 8 * (v >> 2) + (v & 3);
+                    const bool ok = c <= lim_hi && c > lim_lo;
                     sacc[kbk][v] = ok ? sacc[kbk][v] : masked;
                 }
         }
-        float mx = masked;
+        // the row extreme as a tree of 3-way extremes (depth 3, not a chain of
+        // 32 dependent steps)
+        auto e3 = [](float a, float b, float c) __attribute__((always_inline)) {
+            return NEG ? fminf(fminf(a, b), c) : fmaxf(fmaxf(a, b), c);
+        };
+        float part[KB * 4];
 #pragma unroll
         for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) mx = NEG ? fminf(mx, sacc[kbk][v]) : fmaxf(mx, sacc[kbk][v]);
+            for (int i = 0; i < 4; ++i)
+                part[4 * kbk + i] = e3(e3(sacc[kbk][4 * i], sacc[kbk][4 * i + 1], sacc[kbk][4 * i + 2]),
+                                       sacc[kbk][4 * i + 3], masked);
+        float mx = masked;
+#pragma unroll
+        for (int i = 0; i < KB * 4; i += 2) mx = e3(mx, part[i], part[i + 1]);
         const float other = xor32(mx);
         mx = NEG ? fminf(mx, other) : fmaxf(mx, other);
         const float mt = (mx == masked) ? -INFINITY : mx * c2;
@@ -513,7 +529,7 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         }
         __shared__ int sh_part[NW];
         int part = 0;
-        for (int j = tid; j < b; j += 64 * NW) part += (lens[j] + (1 << ps_log2) - 1) >> ps_log2;
+        for (int j = tid; j < b; j += 64 * NW) part += seq_pages(lens[j], ps_log2);
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
         if (lane == 0) sh_part[wave] = part;
@@ -609,7 +625,7 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                 const int page = !any ? 0
                                  : have_pid ? __builtin_amdgcn_readlane(pid, (is_v ? SPW : 0) + i)
                                             : table[off_b + (j0 >> ps_log2)];
-                const uint16_t* tile = (is_v ? V : K) + ((size_t)page * Hkv + g) * ((size_t)ps * D);
+                const uint16_t* tile = (is_v ? V : K) + pool_tile(page, g, Hkv, ps_log2, D);
                 const __amdgpu_buffer_rsrc_t pr =
                     __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, any ? ps * D * 2 : 0, kRsrcWord3);
                 const int j = j0 + (lane >> 4);
