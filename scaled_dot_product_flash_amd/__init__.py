@@ -91,10 +91,20 @@ def _check(rc, what):
         raise RuntimeError(f"{what} failed ({rc}): {strerror(rc)}")
 
 
-def _stream(t):
+def _launch(t, entry, *args):
+    """entry(*args, stream) with t's device current and torch's current stream
+    on that device as the last argument (the device is switched only when it
+    is not already current: the switch costs more than the launch)."""
     import torch
 
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    dev = t.device.index
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if torch.cuda.current_device() != dev:
+        with torch.cuda.device(dev):
+            stream = raw(dev) if raw is not None else torch.cuda.current_stream(dev).cuda_stream
+            return entry(*args, stream)
+    stream = raw(dev) if raw is not None else torch.cuda.current_stream(dev).cuda_stream
+    return entry(*args, stream)
 
 
 def _need(t, name, dtype):
@@ -132,14 +142,12 @@ def _prefill(entry, dtype, q, k, v, o, scale, causal, window, lse=False):
         scale = 1.0 / math.sqrt(D)
     if lse:
         out_lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-        with torch.cuda.device(q.device):
-            rc = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), out_lse.data_ptr(), B, Hq, Hkv,
-                       Sq, Sk, D, float(scale), int(bool(causal)), int(window), _stream(q))
+        rc = _launch(q, entry, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), out_lse.data_ptr(), B, Hq, Hkv,
+                     Sq, Sk, D, float(scale), int(bool(causal)), int(window))
         _check(rc, entry.__name__)
         return o, out_lse
-    with torch.cuda.device(q.device):
-        rc = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, Hq, Hkv, Sq, Sk, D,
-                   float(scale), int(bool(causal)), int(window), _stream(q))
+    rc = _launch(q, entry, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, Hq, Hkv, Sq, Sk, D,
+                 float(scale), int(bool(causal)), int(window))
     _check(rc, entry.__name__)
     return o
 
@@ -205,10 +213,9 @@ def bwd(q, k, v, o, do, lse, scale=None, causal=False, window=0, dq=None, dk=Non
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     lib = load_library()
-    with torch.cuda.device(q.device):
-        rc = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Sq, Sk, D, float(scale),
-                          int(bool(causal)), int(window), _stream(q))
+    rc = _launch(q, lib.attn_bwd, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Sq, Sk, D, float(scale),
+                 int(bool(causal)), int(window))
     _check(rc, "attn_bwd")
     return dq, dk, dv
 
@@ -247,9 +254,8 @@ def decode_paged(q, k_pool, v_pool, page_table, seq_lens, scale=None, o=None):
 
     lib = load_library()
     B, Hq, Hkv, D, ps, scale, o = _decode_args(q, k_pool, v_pool, page_table, seq_lens, scale, o)
-    with torch.cuda.device(q.device):
-        rc = lib.attn_decode_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(),
-                                   seq_lens.data_ptr(), B, Hq, Hkv, D, ps, scale, o.data_ptr(), _stream(q))
+    rc = _launch(q, lib.attn_decode_paged, q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(),
+                 seq_lens.data_ptr(), B, Hq, Hkv, D, ps, scale, o.data_ptr())
     _check(rc, "attn_decode_paged")
     return o
 
@@ -263,10 +269,9 @@ def decode_paged_noalloc(q, k_pool, v_pool, page_table, seq_lens, scale=None, o=
 
     lib = load_library()
     B, Hq, Hkv, D, ps, scale, o = _decode_args(q, k_pool, v_pool, page_table, seq_lens, scale, o)
-    with torch.cuda.device(q.device):
-        rc = lib.attn_decode_paged_noalloc(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
-                                           page_table.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, ps, scale,
-                                           o.data_ptr(), _stream(q))
+    rc = _launch(q, lib.attn_decode_paged_noalloc, q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                 page_table.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, ps, scale,
+                 o.data_ptr())
     _check(rc, "attn_decode_paged_noalloc")
     return o
 
@@ -278,10 +283,9 @@ def decode_paged_window(q, k_pool, v_pool, page_table, seq_lens, window, scale=N
 
     lib = load_library()
     B, Hq, Hkv, D, ps, scale, o = _decode_args(q, k_pool, v_pool, page_table, seq_lens, scale, o)
-    with torch.cuda.device(q.device):
-        rc = lib.attn_decode_paged_window(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
-                                          page_table.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, ps, scale,
-                                          int(window), o.data_ptr(), _stream(q))
+    rc = _launch(q, lib.attn_decode_paged_window, q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                 page_table.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, ps, scale,
+                 int(window), o.data_ptr())
     _check(rc, "attn_decode_paged_window")
     return o
 
@@ -303,10 +307,8 @@ def kv_append(k_new, v_new, k_pool, v_pool, page_table, seq_lens):
     B, Hkv, D = k_new.shape
     if k_pool.shape[1] != Hkv or k_pool.shape[3] != D or seq_lens.shape != (B,):
         raise ValueError("k_new, the pools and seq_lens do not match")
-    with torch.cuda.device(k_new.device):
-        rc = lib.attn_kv_append(k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
-                                page_table.data_ptr(), seq_lens.data_ptr(), B, Hkv, D, k_pool.shape[2],
-                                _stream(k_new))
+    rc = _launch(k_new, lib.attn_kv_append, k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                 page_table.data_ptr(), seq_lens.data_ptr(), B, Hkv, D, k_pool.shape[2])
     _check(rc, "attn_kv_append")
 
 
@@ -386,9 +388,8 @@ def fwd_paged(q, k_pool, v_pool, page_table, seq_lens, o=None, scale=None, causa
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     out_lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if lse else None
-    with torch.cuda.device(q.device):
-        rc = lib.attn_fwd_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(),
-                                seq_lens.data_ptr(), o.data_ptr(), out_lse.data_ptr() if lse else None, B, Hq, Hkv,
-                                Sq, D, ps, float(scale), int(bool(causal)), int(window), _stream(q))
+    rc = _launch(q, lib.attn_fwd_paged, q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(),
+                 seq_lens.data_ptr(), o.data_ptr(), out_lse.data_ptr() if lse else None, B, Hq, Hkv,
+                 Sq, D, ps, float(scale), int(bool(causal)), int(window))
     _check(rc, "attn_fwd_paged")
     return (o, out_lse) if lse else o
