@@ -24,7 +24,13 @@ oracle over the whole prefill workload and the whole decode workload on the
 host cores (a pool of single-threaded worker processes, at most 16).
 Before the warmup, the step runs back to back for ``--settle-ms`` so that no
 timed step sees the clock ramp of an idle GPU; the headline is the median
-launch, with mean, standard deviation and minimum beside it.
+launch, with mean, standard deviation and minimum beside it. ``counters``
+holds what rocprofv3 --pmc reads on a child run of the step: the prefill
+kernel's MFMA utilisation (SQ_VALU_MFMA_BUSY_CYCLES over the cycles of its
+SIMDs) and the HBM bytes and GB/s of both kernels (FETCH_SIZE and WRITE_SIZE
+scaled by what they read for a plain device copy); ``roofline.traffic`` comes
+from there (from the committed profile summary when the passes cannot run,
+e.g. under ``--no-counters``).
 Progress goes to stderr.
 """
 
@@ -188,7 +194,183 @@ def cpu_baseline(pool, n, p_flops, d_bytes):
     }
 
 
+# ---- hardware counters: rocprofv3 --pmc over a child run of the step ----
+# Two passes (the TCC block holds FETCH_SIZE or WRITE_SIZE, not both). The
+# child runs the step's two calls and one plain 256 MiB device copy per step,
+# a few times after a short settle; the copy gives each byte counter's scale.
+
+COUNTER_PASSES = (
+    ("FETCH_SIZE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE"),
+    ("WRITE_SIZE",),
+)
+COUNTER_STEPS = 3
+COPY_BYTES = 256 << 20
+
+
+def _rocprofv3():
+    import shutil
+
+    p = shutil.which("rocprofv3")
+    if p is None and os.path.exists("/opt/rocm/bin/rocprofv3"):
+        p = "/opt/rocm/bin/rocprofv3"
+    return p
+
+
+def _pmc_pass(prof, counters, timeout_s=240):
+    """One rocprofv3 --pmc pass over `bench.py --counter-child`; returns
+    {kernel name: [per-dispatch {counter: value, "dur_ns": ...}]} in dispatch
+    order, or raises RuntimeError."""
+    import csv
+    import glob
+    import shutil
+    import signal
+    import subprocess
+    import tempfile
+
+    d = tempfile.mkdtemp(prefix="attn_pmc_", dir="/tmp")
+    cmd = [prof, "--pmc", *counters, "-d", d, "-o", "run", "--output-format", "csv", "--",
+           sys.executable, os.path.abspath(__file__), "--counter-child"]
+    env = dict(os.environ, TMPDIR="/tmp")
+    try:
+        proc = subprocess.Popen(cmd, cwd="/tmp", env=env, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE,
+                                start_new_session=True)
+        try:
+            _, err = proc.communicate(timeout=timeout_s)
+        except subprocess.TimeoutExpired:
+            os.killpg(proc.pid, signal.SIGKILL)
+            proc.communicate()
+            raise RuntimeError(f"rocprofv3 --pmc {' '.join(counters)}: no result within {timeout_s} s")
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            tail = err.decode(errors="replace").strip().splitlines()[-1:] if err else []
+            raise RuntimeError(f"rocprofv3 --pmc {' '.join(counters)} exited {proc.returncode} without a counter "
+                               f"file {tail}")
+        per = {}
+        with open(files[0]) as f:
+            for row in csv.DictReader(f):
+                rec = per.setdefault(row["Kernel_Name"], {}).setdefault(int(row["Dispatch_Id"]), {})
+                rec[row["Counter_Name"]] = float(row["Counter_Value"])
+                rec["dur_ns"] = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+        return {k: [v[i] for i in sorted(v)] for k, v in per.items()}
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+
+
+def hardware_counters(num_cu):
+    """MFMA utilisation of the prefill kernel and HBM bytes of the prefill
+    and decode kernels, from rocprofv3 --pmc passes over a child run of the
+    step. Byte counters are scaled by what they read for the plain copy."""
+    prof = _rocprofv3()
+    if prof is None:
+        return {"error": "rocprofv3 not found"}
+    try:
+        passes = [_pmc_pass(prof, c) for c in COUNTER_PASSES]
+    except (RuntimeError, OSError, ValueError, KeyError) as e:
+        return {"error": str(e)}
+    return summarize_counters(passes[0], passes[1], num_cu)
+
+
+def summarize_counters(fpass, wpass, num_cu):
+    """The counters object from the two passes' per-kernel dispatch records
+    ({kernel name: [{counter: value, "dur_ns": ns}, ...]})."""
+
+    def last(per, sub, key):
+        names = [n for n in per if sub in n]
+        if not names:
+            raise KeyError(f"no {sub} dispatch")
+        name = max(names, key=lambda n: len(per[n]))
+        recs = per[name][-COUNTER_STEPS:]
+        return name, sum(r[key] for r in recs) / len(recs), sum(r["dur_ns"] for r in recs) / len(recs)
+
+    def copy_scale(per, key):
+        recs = [r for n, v in per.items() if "copyBuffer" in n for r in v if r.get(key, 0.0) > 1024.0]
+        if not recs:
+            raise KeyError("no copy dispatch")
+        return (COPY_BYTES / 1024.0) / (sum(r[key] for r in recs) / len(recs))
+
+    try:
+        fs, ws = copy_scale(fpass, "FETCH_SIZE"), copy_scale(wpass, "WRITE_SIZE")
+        pname, p_fetch, p_dur = last(fpass, "prefill_pipe_kernel", "FETCH_SIZE")
+        _, p_write, _ = last(wpass, "prefill_pipe_kernel", "WRITE_SIZE")
+        _, busy, _ = last(fpass, "prefill_pipe_kernel", "SQ_VALU_MFMA_BUSY_CYCLES")
+        _, nmfma, _ = last(fpass, "prefill_pipe_kernel", "SQ_INSTS_MFMA")
+        _, gui, _ = last(fpass, "prefill_pipe_kernel", "GRBM_GUI_ACTIVE")
+        sname, s_fetch, s_dur = last(fpass, "decode_split_kernel", "FETCH_SIZE")
+        _, s_write, _ = last(wpass, "decode_split_kernel", "WRITE_SIZE")
+        mname, m_fetch, m_dur = last(fpass, "decode_merge_kernel", "FETCH_SIZE")
+        _, m_write, _ = last(wpass, "decode_merge_kernel", "WRITE_SIZE")
+    except (KeyError, ValueError, ZeroDivisionError) as e:
+        return {"error": f"counter files incomplete: {e}"}
+    cycles = gui / 8.0                      # GRBM_GUI_ACTIVE sums the 8 XCDs
+    simds = 4 * num_cu
+    p_bytes = p_fetch * 1024 * fs + p_write * 1024 * ws
+    d_bytes = (s_fetch + m_fetch) * 1024 * fs + (s_write + m_write) * 1024 * ws
+    d_dur = s_dur + m_dur
+    return {
+        "source": f"rocprofv3 --pmc, passes {[' '.join(c) for c in COUNTER_PASSES]}, over a child run of the "
+                  f"step (each: a 300 ms settle, then {COUNTER_STEPS} steps plus a {COPY_BYTES >> 20} MiB device "
+                  f"copy); mean of the last {COUNTER_STEPS} dispatches of each kernel",
+        "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+        "prefill": {
+            "kernel": pname,
+            "duration_us": round(p_dur / 1e3, 2),
+            "clock_ghz": round(cycles / p_dur, 3),
+            "mfma_insts": int(nmfma),
+            "mfma_busy_frac": round(busy / (cycles * simds), 4),
+            "mfma_busy_frac_at_2p4ghz": round(busy / (p_dur * 2.4 * simds), 4),
+            "hbm_fetch_bytes": int(p_fetch * 1024 * fs), "hbm_write_bytes": int(p_write * 1024 * ws),
+            "hbm_bytes": int(p_bytes),
+        },
+        "decode": {
+            "kernels": [sname, mname],
+            "duration_us": round(d_dur / 1e3, 2),
+            "hbm_bytes": int(d_bytes),
+            "hbm_gbps": round(d_bytes / d_dur, 2),
+            "frac_peak": round(d_bytes / d_dur / PEAK_HBM_GBPS, 4),
+        },
+    }
+
+
+def counter_child():
+    """The step kernels under the profiler: settle, then COUNTER_STEPS steps,
+    each followed by a plain device copy of COPY_BYTES."""
+    import torch
+
+    import scaled_dot_product_flash_amd as attn
+    from scaled_dot_product_flash_amd import inputs
+
+    wp, wd = inputs.WORKLOADS[PREFILL], inputs.WORKLOADS[DECODE]
+    q, k, v = inputs.workload_inputs(PREFILL)
+    dd = inputs.workload_inputs(DECODE)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    attn.load_library()
+    pq, pk, pv = (t.to(dev) for t in (q, k, v))
+    po = torch.empty_like(pq)
+    dq, dkp, dvp, dpt, dsl = (dd[n].to(dev) for n in ("q", "k_pool", "v_pool", "page_table", "seq_lens"))
+    do = torch.empty_like(dq)
+    csrc = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    cdst = torch.empty_like(csrc)
+    p_scale, d_scale = 1.0 / math.sqrt(wp["D"]), 1.0 / math.sqrt(wd["D"])
+
+    def step():
+        attn.fwd(pq, pk, pv, o=po, scale=p_scale, causal=True, window=0)
+        attn.decode_paged(dq, dkp, dvp, dpt, dsl, scale=d_scale, o=do)
+
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) < 0.3:
+        step()
+        torch.cuda.synchronize()
+    for _ in range(COUNTER_STEPS):
+        step()
+        cdst.copy_(csrc)
+    torch.cuda.synchronize()
+
+
 def main():
+    if "--counter-child" in sys.argv[1:]:
+        counter_child()
+        return
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -198,6 +380,8 @@ def main():
                     help="untimed steps run back to back for this long before the warmup, so the GPU reaches its "
                          "sustained clocks before any timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-counters", action="store_true",
+                    help="skip the rocprofv3 --pmc passes (needed when bench.py itself runs under a profiler)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="add one plain 256 MiB device copy per step (byte-counter scale for PMC runs)")
     args = ap.parse_args()
@@ -530,6 +714,23 @@ def main():
         "kernels": "bwd_dq_kernel then bwd_dkdv_kernel; scores and dP are computed in both (14*D executed)",
     }
     out["other_prefill"] = other
+    if args.no_counters:
+        out["counters"] = None
+    else:
+        log("hardware counters: rocprofv3 --pmc passes over a child run of the step")
+        hc = hardware_counters(torch.cuda.get_device_properties(dev).multi_processor_count)
+        out["counters"] = hc
+        if "error" in hc:
+            log(f"counters unavailable: {hc['error']}")
+        else:
+            src = "counters (this run): rocprofv3 FETCH_SIZE + WRITE_SIZE per dispatch, scaled by a plain copy"
+            out["roofline"]["traffic"] = hc["prefill"]["hbm_bytes"]
+            out["roofline"]["traffic_source"] = src
+            out["roofline"]["mfma_busy_frac"] = hc["prefill"]["mfma_busy_frac"]
+            out["roofline"]["clock_ghz"] = hc["prefill"]["clock_ghz"]
+            out["decode"]["roofline"]["traffic"] = hc["decode"]["hbm_bytes"]
+            out["decode"]["roofline"]["traffic_source"] = src
+            out["decode"]["roofline"]["counter_gbps"] = hc["decode"]["hbm_gbps"]
     if pool is not None:
         log(f"cpu baseline: the float64 oracle over both workloads, {n_workers} worker processes")
         out["cpu_baseline"] = cpu_baseline(pool, n_workers, p_flops, d_bytes)

@@ -11,10 +11,10 @@
 // row maximum and row sum are kept, earlier partial output is rescaled when
 // the maximum grows, and only O is written back).
 //
-// Two kernels share the gfx950 mapping below: prefill_pipe_kernel (D = 128,
-// eight waves and 256 query rows per workgroup, software pipelined, described
-// above its definition) and prefill_bf16_kernel (D = 64, four waves and 128
-// rows). Common to both:
+// One kernel, prefill_pipe_kernel (software pipelined, described above its
+// definition), for D = 128 (eight waves and 256 query rows per workgroup, or
+// four waves and 128 rows) and D = 64 (four waves and 128 rows, three
+// workgroups per CU). The gfx950 mapping:
 //  * 32 query rows per wave. Each wave computes S^T = K_tile · Q^T with
 //    v_mfma_f32_32x32x16_bf16, so a lane owns one query column and 16 key
 //    rows of each 32-key block; the row maximum of a query is a reduction
@@ -63,11 +63,6 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;  // query rows per workgroup
-
-
 __device__ __forceinline__ uint4 ld_global16(const uint16_t* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
@@ -81,375 +76,16 @@ constexpr int kRsrcWord3 = 0x00020000;
 // Lazy-rescale threshold for the reference maximum, log2 units.
 constexpr float kLazy = 8.0f;
 
-template <int D, bool NEG, bool PAGED>
-__global__ __launch_bounds__(kThreads, 2)
-void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                         const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-                         int Hq, int Hkv, int Sq, int Sk, float c2, int causal, int window,
-                         int nqt, int nitems, int chunk, int pair,
-                         const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int ps_log2) {
-    constexpr int BN = 64;                // keys per tile
-    constexpr int KB = BN / 32;           // 32-key blocks per tile
-    constexpr int KS = BN / 16;           // 16-key MFMA k-steps per tile (P·V)
-    constexpr int DS = D / 16;            // 16-wide d steps (Q·K^T)
-    constexpr int DB = D / 32;            // 32-row d blocks of O^T
-    constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
-    constexpr int TILE_BYTES = BN * D * 2;
-    constexpr int SLOTS = TILE_BYTES / 1024;    // 1 KiB DMA slots per tile and tensor
-    static_assert(SLOTS % kWaves == 0, "DMA slots per wave");
-
-    // two pipeline stages, each its own LDS object
-    __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char k_lds1[TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char v_lds1[TILE_BYTES];
-
-    // ---- work item -------------------------------------------------------
-    const int w = blockIdx.x;
-    const int item = dealt_item(w, chunk, nitems, pair, nqt, Hq / Hkv);
-    if (item < 0) return;
-    const int G = Hq / Hkv;
-    const int hg = item % G;
-    const int r1 = item / G;
-    const int qt = nqt - 1 - (r1 % nqt);
-    const int bg = r1 / nqt;
-    const int g = bg % Hkv;
-    int b = bg / Hkv;
-    const int h = g * G + hg;
-
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
-    const int ln = lane & 31;
-    const int hh = lane >> 5;
-
-    // paged: as in the pipelined kernel, sequence slot b takes the sequence
-    // of b-th largest length (up to 64 * kWaves sequences), then its length
-    // and first page-table entry off_b = sum over j < b of ceil(lens[j] / ps)
-    int off_b = 0;
-    if constexpr (PAGED) {
-        const int B = nitems / (Hq * nqt);
-        if (B <= 64 * kWaves) {
-            __shared__ int sh_seq;
-            if (tid < B) {
-                const int my = lens[tid];
-                int rank = 0;
-                for (int j = 0; j < B; ++j) {
-                    const int lj = lens[j];
-                    rank += (lj > my) || (lj == my && j < tid);
-                }
-                if (rank == b) sh_seq = tid;
-            }
-            __syncthreads();
-            b = sh_seq;
-        }
-        __shared__ int sh_part[kWaves];
-        int part = 0;
-        for (int j = tid; j < b; j += kThreads) part += seq_pages(lens[j], ps_log2);
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m);
-        if (lane == 0) sh_part[wave] = part;
-        __syncthreads();
-#pragma unroll
-        for (int x = 0; x < kWaves; ++x) off_b += sh_part[x];
-        Sk = lens[b];
-        if (Sk < 1) return;   // outside the precondition seq_lens[b] >= 1: nothing to do
-    }
-    const int ps = 1 << ps_log2;
-
-    const int off = Sk - Sq;  // bottom-right causal alignment
-    const int i0 = qt * kBM;
-    const int row_end = min(i0 + kBM, Sq);
-
-    const size_t qo_base = ((size_t)b * Hq + h) * (size_t)Sq * D;
-    const size_t kv_base = PAGED ? 0 : ((size_t)b * Hkv + g) * (size_t)Sk * D;
-    // Buffer resources over this (batch, kv head) slice: rows past Sk read
-    // as zeros instead of outside the slice.
-    const int kv_bytes = PAGED ? 0 : Sk * D * 2;
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(K + kv_base), 0, kv_bytes, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(V + kv_base), 0, kv_bytes, kRsrcWord3);
-
-    // key range of the whole workgroup
-    const int p_first = i0 + off;
-    const int p_last = row_end - 1 + off;
-    const int hi = causal ? min(Sk, p_last + 1) : Sk;
-    const int lo = (causal && window > 0) ? max(0, p_first - window + 1) : 0;
-    const int t_begin = lo / BN;
-    const int t_end = (hi + BN - 1) / BN;
-
-    // key range of this wave
-    const int wr0 = i0 + 32 * wave;
-    const int wr1 = min(wr0 + 32, Sq) - 1;
-    const bool wave_rows = wr0 < Sq;
-    const int wp0 = wr0 + off, wp1 = wr1 + off;
-    const int w_hi = causal ? min(Sk - 1, wp1) : Sk - 1;           // largest visible key
-    const int w_lo = (causal && window > 0) ? max(0, wp0 - window + 1) : 0;
-    const int w_full_hi = causal ? min(Sk - 1, wp0) : Sk - 1;      // visible to every row
-    const int w_full_lo = (causal && window > 0) ? max(0, wp1 - window + 1) : 0;
-
-    // ---- Q in registers (MFMA B operand: column = query, 8 d per lane) ----
-    const int qrow = wr0 + ln;
-    const int qpos = qrow + off;
-    bf16x8 qreg[DS];
-    {
-        const bool ok = qrow < Sq;
-        const uint16_t* qp = Q + qo_base + (size_t)(ok ? qrow : 0) * D + 8 * hh;
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-            uint4 x = ok ? ld_global16(qp + 16 * s) : make_uint4(0, 0, 0, 0);
-            qreg[s] = as_bf16x8(x);
-        }
-    }
-
-    // ---- tile staging: buffer -> LDS DMA, 1 KiB per wave instruction --------
-    // K rows keep their 16-byte chunks XOR-swizzled by kswz(row) and V rows by
-    // vswz(row); the DMA realises the swizzle through the per-lane source
-    // offset because its LDS destination is always base + 16 * lane.
-    auto kswz = [](int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
-    auto vswz = [](int row) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); };
-    auto issue_tile = [&](int t, unsigned char* kdst, unsigned char* vdst) {
-        const int j0 = t * BN;
-#pragma unroll
-        for (int i = 0; i < SLOTS / kWaves; ++i) {
-            const int sl = wave + kWaves * i;
-            const int u = sl * 64 + lane;          // 16-byte unit of the tile
-            const int row = u / CPR, phys = u % CPR;
-            const int kc = phys ^ kswz(row), vcn = phys ^ vswz(row);
-            if constexpr (PAGED) {
-                // the rows of a slot (64 / CPR <= 8 consecutive, starting at a
-                // multiple of that) lie in one page (page_size >= 8); the slot
-                // reads through a buffer resource over its (page, kv head)
-                // tile, and rows at or past Sk read zeros
-                const int r0 = j0 + sl * (64 / CPR);
-                const bool any = r0 < Sk;
-                const int page = any ? table[off_b + (r0 >> ps_log2)] : 0;
-                const size_t tb = pool_tile(page, g, Hkv, ps_log2, D);
-                const int bytes = any ? ps * D * 2 : 0;
-                const __amdgpu_buffer_rsrc_t pk = __builtin_amdgcn_make_buffer_rsrc((void*)(K + tb), 0, bytes, kRsrcWord3);
-                const __amdgpu_buffer_rsrc_t pv = __builtin_amdgcn_make_buffer_rsrc((void*)(V + tb), 0, bytes, kRsrcWord3);
-                const int j = j0 + row;
-                const unsigned rb = (unsigned)((j & (ps - 1)) * D * 2);
-                const bool in = j < Sk;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(pk, (lds_void*)(kdst + sl * 1024), 16,
-                                                         in ? rb + (unsigned)(16 * kc) : (unsigned)(ps * D * 2), 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(pv, (lds_void*)(vdst + sl * 1024), 16,
-                                                         in ? rb + (unsigned)(16 * vcn) : (unsigned)(ps * D * 2), 0, 0, 0);
-            } else {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + sl * 1024), 16,
-                                                         (unsigned)(((j0 + row) * D + 8 * kc) * 2), 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + sl * 1024), 16,
-                                                         (unsigned)(((j0 + row) * D + 8 * vcn) * 2), 0, 0, 0);
-            }
-        }
-    };
-
-    // ---- running state ------------------------------------------------------
-    f32x16 oacc[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
-    // Reference maximum of the scaled logits (log2 units). It only moves when
-    // a tile's maximum exceeds it by more than kLazy, so most tiles skip the
-    // rescale of O; probabilities stay <= 2^kLazy, and because numerator and
-    // denominator share the same reference the result is unchanged.
-    float m_run = -INFINITY;
-    float l_run = 0.f;        // this lane's share of the row sum (of bf16 P)
-    const uint32_t ones = 0x3F803F80u;  // bf16 pair (1, 1)
-
-    // V^T operand reads: a 16-lane group reads 4 keys x 16 d with the
-    // transposing LDS read, lane i of the group receiving d = base + i.
-    const int grp = (lane >> 4) & 1;         // which 16 d of the 32-d block
-    const int e4 = (lane & 15) >> 2;         // key offset within the 4 keys
-    const int q4 = lane & 3;                 // 4-d column group
-    auto vread = [&](const unsigned char* vb, int key, int d) -> s16x4 {
-        const int off_b = key * (D * 2) + (((d >> 3) ^ vswz(key)) << 4) + ((d & 7) << 1);
-        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + off_b));
-    };
-
-    // One K/V tile: S^T = K·Q^T, online softmax, O^T += V^T·P^T. `edge` tiles
-    // straddle a mask boundary or the key tail; only they evaluate the mask,
-    // in two wave-uniform branches the other tiles jump over.
-    auto tile = [&](const unsigned char* kb, const unsigned char* vb, int j0, bool edge) {
-        f32x16 sacc[KB];
-#pragma unroll
-        for (int kbk = 0; kbk < KB; ++kbk)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) sacc[kbk][v] = 0.f;
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-#pragma unroll
-            for (int kbk = 0; kbk < KB; ++kbk) {
-                const int key = 32 * kbk + ln;
-                const int cc = 2 * s + hh;
-                const uint4 a = *reinterpret_cast<const uint4*>(kb + key * (D * 2) + ((cc ^ kswz(key)) << 4));
-                sacc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qreg[s], sacc[kbk], 0, 0, 0);
-            }
-        }
-
-        // edge tiles: masked logits become -inf (+inf for a negative scale), so
-        // they never win the extreme and exp2 turns them into exact zeros. The
-        // empty volatile asm keeps this block a real branch: the compiler may
-        // not speculate it into every tile.
-        const float masked = NEG ? INFINITY : -INFINITY;
-        if (edge) {
-            asm volatile("");
-            // key j0 + base + c is visible iff c <= lim_hi and c > lim_lo, with
-            // c the value's compile-time column in the tile: one compare per
-            // bound and value
-            const int base = j0 + 4 * hh;
-            const int sk_hi = Sk - 1 - base;
-            const int lim_hi = causal ? min(qpos - base, sk_hi) : sk_hi;
-            const int lim_lo = window > 0 ? qpos - window - base : -1;
-#pragma unroll
-            for (int kbk = 0; kbk < KB; ++kbk)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int c = 32 * kbk + 8 * (v >> 2) + (v & 3);
-                    const bool ok = c <= lim_hi && c > lim_lo;
-                    sacc[kbk][v] = ok ? sacc[kbk][v] : masked;
-                }
-        }
-        // the row extreme as a tree of 3-way extremes (depth 3, not a chain of
-        // 32 dependent steps)
-        auto e3 = [](float a, float b, float c) __attribute__((always_inline)) {
-            return NEG ? fminf(fminf(a, b), c) : fmaxf(fmaxf(a, b), c);
-        };
-        float part[KB * 4];
-#pragma unroll
-        for (int kbk = 0; kbk < KB; ++kbk)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                part[4 * kbk + i] = e3(e3(sacc[kbk][4 * i], sacc[kbk][4 * i + 1], sacc[kbk][4 * i + 2]),
-                                       sacc[kbk][4 * i + 3], masked);
-        float mx = masked;
-#pragma unroll
-        for (int i = 0; i < KB * 4; i += 2) mx = e3(mx, part[i], part[i + 1]);
-        const float other = xor32(mx);
-        mx = NEG ? fminf(mx, other) : fmaxf(mx, other);
-        const float mt = (mx == masked) ? -INFINITY : mx * c2;
-
-        // move the reference maximum only when this tile exceeds it by kLazy
-        const bool need = mt > m_run + kLazy;
-        if (__builtin_amdgcn_ballot_w64(need)) {
-            // lanes that keep their reference scale by 1 (m_run may still be
-            // -inf there, and -inf - -inf would be NaN); a first finite
-            // maximum scales by exp2(-inf) = 0, clearing nothing but zeros
-            const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
-            m_run = need ? mt : m_run;
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
-        }
-
-        // P = exp2(s * c2 - m); a row with no visible key yet subtracts 0
-        // (its logits here are all masked, so every p is exp2(-inf) = 0)
-        const float msub = (m_run == -INFINITY) ? 0.f : m_run;
-#pragma unroll
-        for (int kbk = 0; kbk < KB; ++kbk)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                sacc[kbk][v] = __builtin_amdgcn_exp2f(fmaf(sacc[kbk][v], c2, -msub));
-
-        // bf16 pairs of P as MFMA B operands; l += the same rounded values
-        bf16x8 pb[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int j = 0; j < 8; j += 2) {
-                const int kbk = ks >> 1, v0 = 8 * (ks & 1) + j;
-                f32x2 pr = {sacc[kbk][v0], sacc[kbk][v0 + 1]};
-                const bf16x2 pbf = __builtin_convertvector(pr, bf16x2);
-                l_run = __builtin_amdgcn_fdot2_f32_bf16(pbf, __builtin_bit_cast(bf16x2, ones), l_run, false);
-                pb[ks][j] = pbf[0];
-                pb[ks][j + 1] = pbf[1];
-            }
-        }
-
-        // O^T += V^T · P^T. For k-step ks (keys 16*ks .. 16*ks+15 of the tile)
-        // the accumulator hands lane-half hh the keys 16ks + 4hh + {0..3} and
-        // 16ks + 8 + 4hh + {0..3}; two transposing reads fetch exactly those.
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int key0 = 16 * ks + 4 * hh + e4;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int d = 32 * db + 16 * grp + 4 * q4;
-                const s16x4 lo4 = vread(vb, key0, d);
-                const s16x4 hi4 = vread(vb, key0 + 8, d);
-                const s16x8 a8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[ks], oacc[db], 0, 0, 0);
-            }
-        }
-    };
-
-    auto step = [&](int t, unsigned char* kcur, unsigned char* vcur, unsigned char* knext, unsigned char* vnext) {
-        if (t + 1 < t_end) issue_tile(t + 1, knext, vnext);
-        const int j0 = t * BN;
-        const bool active = wave_rows && j0 <= w_hi && j0 + BN - 1 >= w_lo;
-        if (active) {
-            const bool edge = (j0 + BN - 1 > w_full_hi) || (j0 < w_full_lo);
-            tile(kcur, vcur, j0, edge);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    };
-
-    issue_tile(t_begin, k_lds0, v_lds0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    for (int t = t_begin; t < t_end; t += 2) {
-        step(t, k_lds0, v_lds0, k_lds1, v_lds1);
-        if (t + 1 < t_end) step(t + 1, k_lds1, v_lds1, k_lds0, v_lds0);
-    }
-
-    // ---- epilogue: O = O^T / l in bf16, through LDS to whole-row stores ----
-    if (!wave_rows) return;
-    const float l_tot = l_run + xor32(l_run);
-    const float inv = 1.f / l_tot;
-    // log-sum-exp of the scaled logits, natural log: sum_j exp(scale s_j)
-    // = 2^m_ref * l with m_ref the reference maximum in log2 units
-    if (LSE != nullptr && hh == 0 && qrow < Sq)
-        LSE[((size_t)b * Hq + h) * Sq + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
-    // The wave's 32 x D block (half a K/V tile buffer, free after the last
-    // barrier) is written in the accumulator layout, 8 bytes per (row, four
-    // d), and read back as whole rows, so each store instruction writes
-    // 64 / CPR contiguous rows. 16-byte chunks are XOR-swizzled by row.
-    unsigned char* stage = ((wave >> 1) == 0 ? k_lds0 : v_lds0) + (wave & 1) * (32 * D * 2);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            f32x2 a = {oacc[db][4 * r + 0] * inv, oacc[db][4 * r + 1] * inv};
-            f32x2 c = {oacc[db][4 * r + 2] * inv, oacc[db][4 * r + 3] * inv};
-            uint2 st;
-            st.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2));
-            st.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(c, bf16x2));
-            const int chunk = (4 * db + r) ^ (ln & (CPR - 1));
-            *reinterpret_cast<uint2*>(stage + ln * (D * 2) + chunk * 16 + hh * 8) = st;
-        }
-    wave_lds_fence();
-    const int cl = lane % CPR;
-#pragma unroll
-    for (int i = 0; i < CPR / 2; ++i) {
-        const int row = i * (64 / CPR) + lane / CPR;
-        const uint4 x = *reinterpret_cast<const uint4*>(stage + row * (D * 2) + ((cl ^ (row & (CPR - 1))) << 4));
-        if (wr0 + row < Sq) *reinterpret_cast<uint4*>(O + qo_base + (size_t)(wr0 + row) * D + 8 * cl) = x;
-    }
-}
-
 // ---------------------------------------------------------------------------
-// D = 128, software pipelined. Per wave and K/V tile t, one basic block holds
-//  * an S phase of eight chunks: two MFMAs of S(t+1) = K(t+1)·Q^T (their K
-//    operands read from LDS two chunks ahead) beside the exp2 / bf16
+// Software pipelined. Per wave and K/V tile t, one basic block holds
+//  * an S phase of eight chunks: D/64 MFMAs per chunk of S(t+1) = K(t+1)·Q^T
+//    (their K operands read from LDS a chunk ahead) beside the exp2 / bf16
 //    conversion of one eighth of P(t), so the matrix and vector units work at
 //    the same time;
-//  * a P·V phase of four chunks: four MFMAs of O^T += V(t)^T·P(t)^T (the
-//    transposing V reads one chunk ahead) beside the mask (boundary tiles
-//    only) and row maximum of S(t+1), and the lazy move of the reference
-//    maximum for tile t+1.
+//  * a P·V phase (chunks 2-9): D/64 MFMAs per chunk of O^T += V(t)^T·P(t)^T
+//    (the transposing V reads one chunk ahead) beside the row maximum of
+//    S(t+1); the mask of a boundary tile and the lazy move of the reference
+//    maximum for tile t+1 follow the block.
 // The O rescale that a moved maximum asks for runs at the start of the next
 // step, in a branch taken only when some lane of the wave needs it.
 // sched_barrier fences keep the chunks in this order; inside a chunk the
@@ -457,7 +93,9 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
 // block 0 second, while P(t) consumes block 0 first: only three of the four
 // 16-register blocks of S(t) and S(t+1) are live at any time.
 // K is staged one tile ahead of V: during step t the LDS holds K(t+1) and
-// V(t) while the DMA fills K(t+2) and V(t+1).
+// V(t) while the DMA fills K(t+2) and V(t+1); the step's DMA goes out after
+// chunk 1 of the block rather than right after the barrier, where every wave
+// of the CU would issue its share at the same moment.
 
 __device__ __forceinline__ float2 halves(float x) {
     // lanes l and l ^ 32 of x, in every lane (v_permlane32_swap)
@@ -469,14 +107,18 @@ __device__ __forceinline__ float2 halves(float x) {
 // PAGED: K and V come from a paged cache ([pages, Hkv, ps, D] pools, a
 // ragged page table and per-sequence lengths, the layout of the paged decode)
 // instead of [B, Hkv, Sk, D] slices; Sk is then the sequence's length.
-template <int NW, bool NEG, bool PAGED>
-__global__ __launch_bounds__(64 * NW, 2)
+template <int NW, int D, bool NEG, bool PAGED>
+__global__ __launch_bounds__(64 * NW, D == 64 ? 3 : 2)
 void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
                          int Hq, int Hkv, int Sq, int Sk, float c2, int causal, int window,
                          int nqt, int nitems, int chunk, int pair,
                          const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int ps_log2) {
-    constexpr int D = 128, BN = 64, KB = 2, KS = 4, DS = 8, DB = 4, CPR = 16;
+    static_assert(D == 64 || D == 128, "head dimension");
+    constexpr int BN = 64, KB = 2, KS = 4, DS = D / 16, DB = D / 32, CPR = D / 8;
+    constexpr int RPS = 1024 / (D * 2);   // K/V rows per 1 KiB DMA slot
+    constexpr int SPC = DS / 4;           // S-steps of S(t+1) per chunk and block
+    constexpr int DPC = DB / 2;           // d blocks of O per P·V chunk
     constexpr int TILE_BYTES = BN * D * 2;
     constexpr int SLOTS = TILE_BYTES / 1024;
     constexpr int BMW = 32 * NW;  // query rows per workgroup
@@ -576,24 +218,32 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     const int qpos = qrow + off;
     bf16x8 qreg[DS];
 
-    // K rows keep their 16-byte chunks XOR-swizzled by (row & 15), V rows by
-    // (row & 3) << 2; the DMA realises the swizzle through the source offset
-    // 1 KiB per wave instruction; slot i of a wave covers rows 16i + (4 wave
-    // + lane/16), so the swizzle (low row bits) and the lane's byte offset are
-    // the same for every slot. The whole offset goes in the VGPR operand,
-    // which the buffer range check covers; the row part is made opaque so the
-    // compiler adds it per tile instead of keeping one VGPR per slot.
-    const int dma_row = 4 * wave + (lane >> 4);
+    // K rows keep their 16-byte chunks XOR-swizzled by kswz(row), V rows by
+    // vswz(row) (D = 128: row & 15 and (row & 3) << 2; D = 64, 8 chunks per
+    // row: (row >> 1) & 7 and ((row >> 1) & 1) << 2), so the MFMA operand
+    // reads of 32 rows at one column and the transposing V reads hit
+    // distinct banks; the DMA realises the swizzle through the source offset.
+    // 1 KiB per wave instruction holds RPS rows (4 at D = 128, 8 at D = 64);
+    // slot i of a wave covers rows RPS (NW i + wave) + lane / CPR, so the
+    // swizzle (low row bits) and the lane's byte offset are the same for
+    // every slot. The whole offset goes in the VGPR operand, which the buffer
+    // range check covers; the row part is made opaque so the compiler adds it
+    // per tile instead of keeping one VGPR per slot.
+    auto kswz = [](int row) __attribute__((always_inline)) { return D == 128 ? (row & 15) : ((row >> 1) & 7); };
+    auto vswz = [](int row) __attribute__((always_inline)) {
+        return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+    };
+    const int dma_row = RPS * wave + lane / CPR;
     static_assert(SLOTS / NW >= 1, "DMA slots");
-    const unsigned kv_lane_k = (unsigned)((dma_row * D + 8 * ((lane & 15) ^ (dma_row & 15))) * 2);
-    const unsigned kv_lane_v = (unsigned)((dma_row * D + 8 * ((lane & 15) ^ ((dma_row & 3) << 2))) * 2);
-    // paged: the four rows of a slot start at a multiple of 4 and so lie in
+    const unsigned kv_lane_k = (unsigned)((dma_row * D + 8 * ((lane % CPR) ^ kswz(dma_row))) * 2);
+    const unsigned kv_lane_v = (unsigned)((dma_row * D + 8 * ((lane % CPR) ^ vswz(dma_row))) * 2);
+    // paged: the RPS rows of a slot start at a multiple of RPS and so lie in
     // one page (page_size >= 8); the slot gets a buffer resource over that
     // (page, kv head) tile, and rows at or past Sk (or a slot wholly past it,
     // whose page is not even looked up) read zeros through the range check
     const int ps = 1 << ps_log2;
-    const unsigned pg_lane_k = (unsigned)((8 * ((lane & 15) ^ (dma_row & 15))) * 2);
-    const unsigned pg_lane_v = (unsigned)((8 * ((lane & 15) ^ ((dma_row & 3) << 2))) * 2);
+    const unsigned pg_lane_k = (unsigned)((8 * ((lane % CPR) ^ kswz(dma_row))) * 2);
+    const unsigned pg_lane_v = (unsigned)((8 * ((lane % CPR) ^ vswz(dma_row))) * 2);
     // paged: the page ids of the slots a wave loads in the next step are
     // fetched one step ahead by a vector load (lane i < SPW: K slot i of tile
     // tk; lane SPW + i: V slot i of tile tv) and taken back with readlane. A
@@ -608,7 +258,7 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                 const bool v_slot = lane >= SPW;
                 const int i = v_slot ? lane - SPW : lane;
                 const int tt = v_slot ? tv : tk;
-                const int j0 = tt * BN + 4 * NW * i + 4 * wave;
+                const int j0 = tt * BN + RPS * NW * i + RPS * wave;
                 if (tt < t_end && j0 < Sk) id = table[off_b + (j0 >> ps_log2)];
             }
         }
@@ -620,7 +270,7 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         for (int i = 0; i < SLOTS / NW; ++i) {
             const int sl = wave + NW * i;
             if constexpr (PAGED) {
-                const int j0 = t * BN + 4 * NW * i + 4 * wave;     // first row of the slot
+                const int j0 = t * BN + RPS * NW * i + RPS * wave;     // first row of the slot
                 const bool any = j0 < Sk;
                 const int page = !any ? 0
                                  : have_pid ? __builtin_amdgcn_readlane(pid, (is_v ? SPW : 0) + i)
@@ -628,12 +278,12 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                 const uint16_t* tile = (is_v ? V : K) + pool_tile(page, g, Hkv, ps_log2, D);
                 const __amdgpu_buffer_rsrc_t pr =
                     __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, any ? ps * D * 2 : 0, kRsrcWord3);
-                const int j = j0 + (lane >> 4);
+                const int j = j0 + lane / CPR;
                 const unsigned voff = j < Sk ? (unsigned)((j & (ps - 1)) * D * 2) + (is_v ? pg_lane_v : pg_lane_k)
                                              : (unsigned)(ps * D * 2);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(pr, (lds_void*)(dst + sl * 1024), 16, voff, 0, 0, 0);
             } else {
-                unsigned rows = (unsigned)((t * BN + 4 * NW * i) * D * 2);
+                unsigned rows = (unsigned)((t * BN + RPS * NW * i) * D * 2);
 #if defined(__HIP_DEVICE_COMPILE__)
                 asm volatile("" : "+s"(rows));
 #endif
@@ -646,7 +296,7 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     auto kread = [&](const unsigned char* kb, int st, int kbk) __attribute__((always_inline)) -> bf16x8 {
         const int key = 32 * kbk + ln;
         const int cc = 2 * st + hh;
-        return as_bf16x8(*reinterpret_cast<const uint4*>(kb + key * (D * 2) + ((cc ^ (key & 15)) << 4)));
+        return as_bf16x8(*reinterpret_cast<const uint4*>(kb + key * (D * 2) + ((cc ^ kswz(key)) << 4)));
     };
     // V^T operand of P·V k-step ks, d block db: for k-step ks the S^T
     // accumulators hand lane half hh the keys 16ks + 4hh + {0..3} and
@@ -657,7 +307,7 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     auto vop = [&](const unsigned char* vb, int ks, int db) __attribute__((always_inline)) -> bf16x8 {
         const int key0 = 16 * ks + 4 * hh + e4;
         const int d = 32 * db + 16 * grp + 4 * q4;
-        const int o_lo = key0 * (D * 2) + (((d >> 3) ^ ((key0 & 3) << 2)) << 4) + ((d & 7) << 1);
+        const int o_lo = key0 * (D * 2) + (((d >> 3) ^ vswz(key0)) << 4) + ((d & 7) << 1);
         const int o_hi = o_lo + 8 * (D * 2);  // key0 + 8 has the same swizzle
         const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + o_lo));
         const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + o_hi));
@@ -740,10 +390,10 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     // caller ahead of the step's DMA issue so their LDS latency overlaps it
     auto kfirst = [&](const unsigned char* kb, bf16x8 (&kr)[4]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) kr[i] = kread(kb, i, 1);
+        for (int i = 0; i < SPC; ++i) kr[i] = kread(kb, i, 1);
     };
     auto main_block = [&](auto next_c, const unsigned char* kb, const unsigned char* vb,
-                          f32x16 (&scur)[KB], f32x16 (&snew)[KB], bf16x8 (&kr)[4]) __attribute__((always_inline)) {
+                          f32x16 (&scur)[KB], f32x16 (&snew)[KB], bf16x8 (&kr)[4], auto&& dma) __attribute__((always_inline)) {
         constexpr bool NEXT = decltype(next_c)::value;
         apply_rescale();
         const float msub = (m_run == -INFINITY) ? 0.f : m_run;
@@ -757,27 +407,31 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         // (c-2)/2, d blocks 2((c-2)%2) and 2((c-2)%2)+1, V read one chunk
         // ahead). The extreme of S(t+1) block 1 runs in chunks 6-7, block 0
         // (whose last MFMA issues in chunk 7) in chunk 9.
-        auto kst = [](int c, int i) __attribute__((always_inline)) { return 2 * (c & 3) + i; };
+        auto kst = [](int c, int i) __attribute__((always_inline)) { return SPC * (c & 3) + i; };
         auto kblk = [](int c) __attribute__((always_inline)) { return 1 - (c >> 2); };
         auto vread2 = [&](int c, bf16x8 (&dst)[2]) __attribute__((always_inline)) {
-            const int ks = (c - 2) >> 1, db0 = 2 * ((c - 2) & 1);
-            dst[0] = vop(vb, ks, db0);
-            dst[1] = vop(vb, ks, db0 + 1);
+            const int ks = (c - 2) >> 1, db0 = DPC * ((c - 2) & 1);
+#pragma unroll
+            for (int i = 0; i < DPC; ++i) dst[i] = vop(vb, ks, db0 + i);
         };
 #pragma unroll
         for (int c = 0; c < 10; ++c) {
             __builtin_amdgcn_sched_barrier(0);
+            if (c == 2) {
+                dma();
+                __builtin_amdgcn_sched_barrier(0);
+            }
             if constexpr (NEXT) {
                 if (c + 1 < 8) {
 #pragma unroll
-                    for (int i = 0; i < 2; ++i) kr[2 * ((c + 1) & 1) + i] = kread(kb, kst(c + 1, i), kblk(c + 1));
+                    for (int i = 0; i < SPC; ++i) kr[SPC * ((c + 1) & 1) + i] = kread(kb, kst(c + 1, i), kblk(c + 1));
                 }
                 if (c < 8) {
                     const int kbs = kblk(c);
 #pragma unroll
-                    for (int i = 0; i < 2; ++i) {
+                    for (int i = 0; i < SPC; ++i) {
                         const f32x16 zero = {};
-                        snew[kbs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[2 * (c & 1) + i], qreg[kst(c, i)],
+                        snew[kbs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[SPC * (c & 1) + i], qreg[kst(c, i)],
                                                                             ((c & 3) == 0 && i == 0) ? zero : snew[kbs],
                                                                             0, 0, 0);
                     }
@@ -785,9 +439,9 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             }
             if (c + 1 >= 2 && c + 1 < 10) vread2(c + 1, vr[(c + 1) & 1]);
             if (c >= 2) {
-                const int ks = (c - 2) >> 1, db0 = 2 * ((c - 2) & 1);
+                const int ks = (c - 2) >> 1, db0 = DPC * ((c - 2) & 1);
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+                for (int i = 0; i < DPC; ++i)
                     oacc[db0 + i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[c & 1][i], pb[ks], oacc[db0 + i], 0, 0, 0);
             }
             if (c < 8) {
@@ -835,10 +489,12 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                     unsigned char* vdst, f32x16 (&scur)[KB], f32x16 (&snew)[KB]) __attribute__((always_inline)) {
         bf16x8 kr[4];
         kfirst(kb, kr);
-        if (t + 2 < t_end) issue(krs, t + 2, kdst, false, pid, PAGED);
-        issue(vrs, t + 1, vdst, true, pid, PAGED);
-        if constexpr (PAGED) pid = page_ids(t + 3, t + 2);
-        float mx = main_block(T{}, kb, vb, scur, snew, kr);
+        auto dma = [&]() __attribute__((always_inline)) {
+            if (t + 2 < t_end) issue(krs, t + 2, kdst, false, pid, PAGED);
+            issue(vrs, t + 1, vdst, true, pid, PAGED);
+            if constexpr (PAGED) pid = page_ids(t + 3, t + 2);
+        };
+        float mx = main_block(T{}, kb, vb, scur, snew, kr, dma);
         if (is_edge(t + 1)) mx = edge_extreme(snew, (t + 1) * BN);
         settle(mx);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -850,7 +506,7 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         if (u + 2 < t_end) issue(krs, u + 2, kdst, false, pid, PAGED);
         if (u + 1 < t_end) issue(vrs, u + 1, vdst, true, pid, PAGED);
         bf16x8 kr[4];
-        main_block(F{}, k_lds0, vb, scur, scur, kr);
+        main_block(F{}, k_lds0, vb, scur, scur, kr, []() {});
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     };
@@ -956,7 +612,7 @@ void prefill_pipe_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     }
 }
 
-template <int NW, bool NEG, bool PAGED>
+template <int NW, int D, bool NEG, bool PAGED>
 hipError_t launch_pipe(const PrefillArgs& a, hipStream_t stream) {
     const int nqt = (a.Sq + 32 * NW - 1) / (32 * NW);
     const long long nitems = (long long)a.B * a.Hq * nqt;
@@ -970,31 +626,8 @@ hipError_t launch_pipe(const PrefillArgs& a, hipStream_t stream) {
     // waves: two workgroups per CU, eight waves: one)
     const int pair = PAGED ? 0
                            : balance_arg(nitems, deal.chunk, (long long)(a.Hq / a.Hkv) * nqt, deal.grid, a.causal,
-                                         a.num_cu, NW == 4 ? 2 : 1);
-    hipLaunchKernelGGL((prefill_pipe_kernel<NW, NEG, PAGED>), dim3((unsigned)deal.grid), dim3(64 * NW), 0, stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                       a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)deal.chunk, pair,
-                       a.page_table, a.seq_lens, ps_log2);
-    return hipGetLastError();
-}
-
-template <int D, bool NEG, bool PAGED>
-hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
-    const int nqt = (a.Sq + kBM - 1) / kBM;
-    const long long nitems = (long long)a.B * a.Hq * nqt;
-    const Deal deal = make_deal(nitems, (long long)(a.Hq / a.Hkv) * nqt, a.Hq / a.Hkv, PAGED);
-    if (!grid_fits(deal.grid, kThreads)) return hipErrorInvalidValue;
-    // causal items: order by weight (three workgroups per CU)
-    const int pair = PAGED ? 0
-                           : balance_arg(nitems, deal.chunk, (long long)(a.Hq / a.Hkv) * nqt, deal.grid, a.causal,
-                                         a.num_cu, 3);
-    float c2 = a.scale * 1.4426950408889634f;
-    // scale 0: a tiny positive factor gives bit-identical weights (all
-    // exp2(0) = 1 for finite logits) and keeps masked logits at -inf
-    if (c2 == 0.f) c2 = 1e-30f;
-    int ps_log2 = 0;
-    while ((1 << ps_log2) < a.page_size) ++ps_log2;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, NEG, PAGED>), dim3((unsigned)deal.grid), dim3(kThreads), 0, stream,
+                                         a.num_cu, NW == 8 ? 1 : D == 64 ? 3 : 2);
+    hipLaunchKernelGGL((prefill_pipe_kernel<NW, D, NEG, PAGED>), dim3((unsigned)deal.grid), dim3(64 * NW), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                        a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)deal.chunk, pair,
                        a.page_table, a.seq_lens, ps_log2);
@@ -1014,15 +647,15 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     const long long wg256 = (long long)a.B * a.Hq * ((a.Sq + 255) / 256);
     const bool small = wg256 < 2LL * 256 || (a.page_table == nullptr && a.Sk <= 2048);
     if (a.page_table != nullptr) {  // paged K/V
-        if (a.D == 64) return neg ? launch_t<64, true, true>(a, stream) : launch_t<64, false, true>(a, stream);
-        if (small) return neg ? launch_pipe<4, true, true>(a, stream) : launch_pipe<4, false, true>(a, stream);
-        return neg ? launch_pipe<8, true, true>(a, stream) : launch_pipe<8, false, true>(a, stream);
+        if (a.D == 64) return neg ? launch_pipe<4, 64, true, true>(a, stream) : launch_pipe<4, 64, false, true>(a, stream);
+        if (small) return neg ? launch_pipe<4, 128, true, true>(a, stream) : launch_pipe<4, 128, false, true>(a, stream);
+        return neg ? launch_pipe<8, 128, true, true>(a, stream) : launch_pipe<8, 128, false, true>(a, stream);
     }
     if (a.D == 128) {
-        if (small) return neg ? launch_pipe<4, true, false>(a, stream) : launch_pipe<4, false, false>(a, stream);
-        return neg ? launch_pipe<8, true, false>(a, stream) : launch_pipe<8, false, false>(a, stream);
+        if (small) return neg ? launch_pipe<4, 128, true, false>(a, stream) : launch_pipe<4, 128, false, false>(a, stream);
+        return neg ? launch_pipe<8, 128, true, false>(a, stream) : launch_pipe<8, 128, false, false>(a, stream);
     }
-    return neg ? launch_t<64, true, false>(a, stream) : launch_t<64, false, false>(a, stream);
+    return neg ? launch_pipe<4, 64, true, false>(a, stream) : launch_pipe<4, 64, false, false>(a, stream);
 }
 
 }  // namespace attn
