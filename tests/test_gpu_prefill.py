@@ -99,8 +99,8 @@ def test_full_size_workload_whole_heads(name):
 
 # More causal items than workgroup slots, in (batch, kv head) groups too small
 # to fill two dispatch rounds of an XCD: each XCD then takes its items heaviest
-# query tile first across its groups. One shape per kernel (D = 64; D = 128 with
-# four waves for at most 2048 keys, eight waves beyond). The output starts as
+# query tile first across its groups. One shape per launch shape (D = 64 with
+# four waves; D = 128 with four waves for at most 2048 keys, eight beyond). The output starts as
 # NaN, so a work item that no workgroup took leaves non-finite rows.
 @pytest.mark.parametrize("shape", [(16, 12, 12, 1024, 64), (12, 32, 8, 1024, 128), (2, 16, 16, 4096, 128)])
 def test_weight_ordered_rounds_sampled_rows(shape):

@@ -41,7 +41,7 @@ CASES = [
     ([200, 333, 17], 4, 2, 17, 256, False, 0, 128),   # non-causal
     ([4096, 2500, 3000, 1], 32, 8, 1, 16, True, 0, 128),   # Sq = 1: a decode step
     ([130, 5000], 16, 4, 130, 64, True, 1000, 128),
-    ([300, 64, 129], 8, 2, 64, 16, True, 0, 64),      # D = 64: the 128-row kernel
+    ([300, 64, 129], 8, 2, 64, 16, True, 0, 64),      # D = 64: four waves, eight rows per DMA slot
     ([1000, 700], 12, 12, 256, 8, True, 0, 64),
     ([500, 80], 8, 1, 80, 32, True, 37, 64),
     ([200, 333, 17], 4, 2, 17, 256, False, 0, 64),
@@ -50,7 +50,7 @@ CASES = [
     # 15 chunks leave the second round one short
     ([900, 50, 400, 1200, 47], 6, 3, 40, 16, True, 0, 128),
     # more sequences than the in-kernel longest-first ranking covers (512 for
-    # the 8-wave kernel, 256 for the D = 64 kernel): slots keep batch order
+    # eight waves, 256 for four waves as at D = 64): slots keep batch order
     ([int(x) for x in np.random.default_rng(7).integers(3, 71, 600)], 8, 2, 3, 8, True, 0, 128),
     ([int(x) for x in np.random.default_rng(8).integers(3, 301, 301)], 4, 4, 3, 16, True, 5, 64),
 ]
