@@ -39,6 +39,10 @@
  *     The workspace lock is held from its size check until the call's
  *     kernels are enqueued; two calls that share a (device, stream) run in
  *     the order they were enqueued.
+ *   - Logging: the library prints nothing, except with ATTN_LOG set to a
+ *     value other than "" or "0" in the environment (read once per process):
+ *     then each kernel launch decision (kernel and template arguments,
+ *     shape, grid, work split) is one "[attn] ..." line on stderr.
  */
 #ifndef ATTN_H
 #define ATTN_H

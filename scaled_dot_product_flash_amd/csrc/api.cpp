@@ -7,11 +7,38 @@
 
 #include <cmath>
 #include <algorithm>
+#include <cstdarg>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <map>
 #include <mutex>
 #include <utility>
 #include <vector>
+
+namespace attn {
+
+bool log_enabled() {
+    static const bool on = [] {
+        const char* v = std::getenv("ATTN_LOG");
+        return v != nullptr && v[0] != '\0' && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+void log_dispatch(const char* fmt, ...) {
+    static std::mutex m;
+    char line[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(line, sizeof line, fmt, ap);
+    va_end(ap);
+    std::lock_guard<std::mutex> lock(m);
+    std::fprintf(stderr, "[attn] %s\n", line);
+}
+
+}  // namespace attn
 
 namespace {
 

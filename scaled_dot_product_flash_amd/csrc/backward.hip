@@ -823,6 +823,10 @@ hipError_t launch_d(const BackwardArgs& a, hipStream_t stream) {
         // causal items: order by weight (two workgroups per CU)
         const int pair = balance_arg(nitems, deal.chunk, (long long)G * nqt, grid, a.causal, a.num_cu, 2);
         if (!grid_fits(grid, kThreads)) return hipErrorInvalidValue;
+        if (log_enabled())
+            log_dispatch("bwd_dq_kernel<%d> B=%d Hq=%d Hkv=%d Sq=%d Sk=%d causal=%d window=%d: grid %lld x %d "
+                         "threads, %lld items of %d rows, chunk %lld, balance %d", D, a.B, a.Hq, a.Hkv, a.Sq, a.Sk,
+                         a.causal, a.window, grid, kThreads, nitems, kRows, deal.chunk, pair);
         hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o,
                            (const uint16_t*)a.dout, a.lse, delta, l2, (uint16_t*)a.dq, qt, dot, a.Hq, a.Hkv, a.Sq, a.Sk,
@@ -837,6 +841,10 @@ hipError_t launch_d(const BackwardArgs& a, hipStream_t stream) {
                              : nullptr;
     const long long grid = (long long)nbg * nkt * nsplit;
     if (!grid_fits(grid, 64 * kKvWaves)) return hipErrorInvalidValue;
+    if (log_enabled())
+        log_dispatch("bwd_dkdv_kernel<%d>: grid %lld x %d threads, %d key blocks of %d per (batch, kv head), "
+                     "%d query splits%s", D, grid, 64 * kKvWaves, nkt, kKvKeys, nsplit,
+                     nsplit > 1 ? " + bwd_kv_reduce_kernel" : "");
     hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)grid), dim3(64 * kKvWaves), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                        qt, dot, l2, delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.Hq, a.Hkv, a.Sq, a.Sk, a.scale, c2,

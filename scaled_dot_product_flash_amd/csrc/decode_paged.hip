@@ -732,6 +732,10 @@ int heads_per_group(int G) {
 template <int D, int GH, bool NEG>
 void launch_split(const DecodeArgs& a, int ps_log2, float c2, hipStream_t stream) {
     const int groups = a.Hkv * ((a.Hq / a.Hkv) / GH);
+    if (log_enabled())
+        log_dispatch("decode_split_kernel<%d,%d,%s> B=%d Hq=%d Hkv=%d page_size=%d window=%d: grid %d x %d x %d, "
+                     "%d heads per workgroup, %d context splits", D, GH, NEG ? "neg" : "pos", a.B, a.Hq, a.Hkv,
+                     a.page_size, a.window, a.nsplit, groups, a.B, GH, a.nsplit);
     hipLaunchKernelGGL((decode_split_kernel<D, GH, NEG>), dim3(a.nsplit, groups, a.B), dim3(kThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k_pool, (const uint16_t*)a.v_pool,
                        a.page_table, a.seq_lens, a.ws, a.Hq, a.Hkv, ps_log2, a.nsplit, c2, a.window);
@@ -745,6 +749,10 @@ void launch_mfma(const DecodeArgs& a, int ps_log2, float c2, hipStream_t stream)
     // exp2 of a finite logit is 1) and keeps masked logits at -inf instead of
     // -inf * 0 = NaN
     if (c2 == 0.f) c2 = 1e-30f;
+    if (log_enabled())
+        log_dispatch("decode_mfma_kernel<%d,%s> B=%d Hq=%d Hkv=%d page_size=%d window=%d: grid %d x %d x %d, "
+                     "%d context splits", D, NEG ? "neg" : "pos", a.B, a.Hq, a.Hkv, a.page_size, a.window, a.nsplit,
+                     groups, a.B, a.nsplit);
     hipLaunchKernelGGL((decode_mfma_kernel<D, NEG>), dim3(a.nsplit, groups, a.B), dim3(kThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k_pool, (const uint16_t*)a.v_pool,
                        a.page_table, a.seq_lens, a.ws, a.Hq, a.Hkv, ps_log2, a.nsplit, c2, a.window);
@@ -816,6 +824,9 @@ hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (log_enabled())
+        log_dispatch("decode_merge_kernel<%d>: grid %d x %d threads, %d partials per head", a.D, a.B * a.Hq, a.D,
+                     a.nsplit);
     if (a.D == 128)
         hipLaunchKernelGGL((decode_merge_kernel<128>), dim3(a.B * a.Hq), dim3(128), 0, stream,
                            (const float*)a.ws, (uint16_t*)a.o, a.B, a.Hq, a.nsplit);

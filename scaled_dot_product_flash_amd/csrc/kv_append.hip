@@ -65,6 +65,9 @@ void kv_append_kernel(const uint16_t* __restrict__ k_new, const uint16_t* __rest
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
     int ps_log2 = 0;
     while ((1 << ps_log2) < a.page_size) ++ps_log2;
+    if (log_enabled())
+        log_dispatch("kv_append_kernel B=%d Hkv=%d D=%d page_size=%d: grid %d x %d threads", a.B, a.Hkv, a.D,
+                     a.page_size, a.B, kThreads);
     hipLaunchKernelGGL(kv_append_kernel, dim3(a.B), dim3(kThreads), 0, stream,
                        (const uint16_t*)a.k_new, (const uint16_t*)a.v_new, (uint16_t*)a.k_pool,
                        (uint16_t*)a.v_pool, a.page_table, a.seq_lens, a.Hkv, a.D, ps_log2);

@@ -21,6 +21,11 @@ __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// ATTN_LOG=1 in the environment (read once per process): every launch
+// decision (kernel, grid, work split) goes to stderr as one "[attn]" line.
+bool log_enabled();
+void log_dispatch(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+
 // A dispatch holds the grid size in work-items, 32 bits per dimension.
 inline bool grid_fits(long long workgroups, int threads) {
     return workgroups > 0 && workgroups * (long long)threads < (1LL << 32);

@@ -627,6 +627,12 @@ hipError_t launch_pipe(const PrefillArgs& a, hipStream_t stream) {
     const int pair = PAGED ? 0
                            : balance_arg(nitems, deal.chunk, (long long)(a.Hq / a.Hkv) * nqt, deal.grid, a.causal,
                                          a.num_cu, NW == 8 ? 1 : D == 64 ? 3 : 2);
+    if (log_enabled())
+        log_dispatch("prefill_pipe_kernel<%d,%d,%s,%s> B=%d Hq=%d Hkv=%d Sq=%d Sk=%d causal=%d window=%d%s: "
+                     "grid %lld x %d threads, %lld items of %d rows, chunk %lld, balance %d",
+                     NW, D, NEG ? "neg" : "pos", PAGED ? "paged" : "contiguous", a.B, a.Hq, a.Hkv, a.Sq, a.Sk,
+                     a.causal, a.window, a.lse ? " +lse" : "", deal.grid, 64 * NW, nitems, 32 * NW, deal.chunk,
+                     pair);
     hipLaunchKernelGGL((prefill_pipe_kernel<NW, D, NEG, PAGED>), dim3((unsigned)deal.grid), dim3(64 * NW), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                        a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt, (int)nitems, (int)deal.chunk, pair,

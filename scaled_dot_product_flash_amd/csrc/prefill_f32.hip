@@ -177,6 +177,10 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
     const long long grid = (long long)a.B * a.Hq * nqt;
     if (!grid_fits(grid, kThreads)) return hipErrorInvalidValue;
     const float c2 = a.scale * 1.4426950408889634f;
+    if (log_enabled())
+        log_dispatch("prefill_f32_kernel<%d> B=%d Hq=%d Hkv=%d Sq=%d Sk=%d causal=%d window=%d%s: grid %lld x %d "
+                     "threads, %d rows per workgroup", D, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window,
+                     a.lse ? " +lse" : "", grid, kThreads, kRows);
     hipLaunchKernelGGL((prefill_f32_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
                        a.Hq, a.Hkv, a.Sq, a.Sk, c2, a.causal, a.window, nqt);

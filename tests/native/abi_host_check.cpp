@@ -228,11 +228,31 @@ void page_pool(unsigned seed) {
     attn_pages_destroy(pool);
 }
 
+// one valid call of each launch shape, each of which must launch: the
+// workloads of the bench and the dispatch branches (eight or four waves,
+// D = 64, paged, vector or MFMA decode, backward with split reduction)
+void dispatch_examples() {
+    const long long before = stub_launches();
+    CHECK(attn_fwd(A, A, A, A, 4, 32, 8, 4096, 4096, 128, 0.088f, 1, 0, nullptr) == ATTN_OK, "fwd c3");
+    CHECK(attn_fwd(A, A, A, A, 8, 12, 12, 1024, 1024, 64, 0.125f, 1, 0, nullptr) == ATTN_OK, "fwd D=64");
+    CHECK(attn_fwd(A, A, A, A, 1, 16, 16, 2048, 2048, 128, -0.088f, 1, 512, nullptr) == ATTN_OK, "fwd 4 waves");
+    CHECK(attn_fwd_f32(A, A, A, A, 1, 1, 1, 128, 128, 64, 0.125f, 0, 0, nullptr) == ATTN_OK, "fwd f32");
+    CHECK(attn_fwd_paged(A, A, A, AI, AI, A, nullptr, 8, 32, 8, 512, 128, 16, 0.088f, 1, 0, nullptr) == ATTN_OK,
+          "fwd paged");
+    CHECK(attn_decode_paged(A, A, A, AI, AI, 64, 32, 8, 128, 16, 0.088f, A, nullptr) == ATTN_OK, "decode");
+    CHECK(attn_decode_paged(A, A, A, AI, AI, 8, 64, 8, 128, 16, 0.088f, A, nullptr) == ATTN_OK, "decode mfma");
+    const float* const AF = reinterpret_cast<const float*>(A);
+    CHECK(attn_bwd(A, A, A, A, A, AF, A, A, A, 1, 8, 2, 1024, 1024, 128, 0.088f, 1, 0, nullptr) == ATTN_OK, "bwd");
+    CHECK(attn_kv_append(A, A, A, A, AI, AI, 4, 8, 128, 16, nullptr) == ATTN_OK, "append");
+    CHECK(stub_launches() - before >= 12, "dispatch examples launched %lld kernels", stub_launches() - before);
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
     const long long calls = argc > 1 ? std::atoll(argv[1]) : 200000;
     validation();
+    dispatch_examples();
     for (unsigned s = 0; s < 4; ++s) sweep(s, calls / 4);
     page_pool(7);
     page_pool(8);

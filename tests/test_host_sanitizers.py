@@ -77,3 +77,31 @@ def test_host_code_under_sanitizers(host_check):
     assert run.stdout.strip().endswith("host checks ok")
     launches = int(re.search(r"launches (\d+)", run.stdout).group(1))
     assert launches > 50000    # the sweep reached the launchers, not only validation
+
+
+def test_dispatch_log(host_check):
+    """ATTN_LOG=1: each launch decision of the dispatch examples is one
+    "[attn]" line on stderr naming the kernel and its grid."""
+    env = dict(os.environ, ATTN_LOG="1", ASAN_OPTIONS="detect_leaks=1:abort_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    run = subprocess.run([host_check, "0"], capture_output=True, text=True, timeout=600, env=env)
+    assert run.returncode == 0, (run.stdout[-3000:], run.stderr[-3000:])
+    lines = [ln for ln in run.stderr.splitlines() if ln.startswith("[attn] ")]
+    text = "\n".join(lines)
+    for want in ("prefill_pipe_kernel<8,128,pos,contiguous> B=4 Hq=32 Hkv=8 Sq=4096 Sk=4096 causal=1 window=0",
+                 "prefill_pipe_kernel<4,64,pos,contiguous> B=8 Hq=12",
+                 "prefill_pipe_kernel<4,128,neg,contiguous> B=1 Hq=16",
+                 "prefill_pipe_kernel<8,128,pos,paged> B=8 Hq=32",
+                 "prefill_f32_kernel<64> B=1 Hq=1",
+                 "decode_split_kernel<128,4,pos> B=64 Hq=32 Hkv=8",
+                 "decode_mfma_kernel<128,pos> B=8 Hq=64 Hkv=8",
+                 "decode_merge_kernel<128>",
+                 "bwd_dq_kernel<128> B=1 Hq=8 Hkv=2",
+                 "bwd_dkdv_kernel<128>",
+                 "kv_append_kernel B=4 Hkv=8 D=128 page_size=16"):
+        assert want in text, (want, text[-3000:])
+    assert all(" grid " in ln for ln in lines)
+    # without the variable the library prints nothing
+    env.pop("ATTN_LOG")
+    quiet = subprocess.run([host_check, "0"], capture_output=True, text=True, timeout=600, env=env)
+    assert quiet.returncode == 0 and "[attn]" not in quiet.stderr
