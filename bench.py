@@ -216,7 +216,7 @@ def _rocprofv3():
     return p
 
 
-def _pmc_pass(prof, counters, timeout_s=240):
+def _pmc_pass(prof, counters, timeout_s=150):
     """One rocprofv3 --pmc pass over `bench.py --counter-child`; returns
     {kernel name: [per-dispatch {counter: value, "dur_ns": ...}]} in dispatch
     order, or raises RuntimeError."""
