@@ -406,12 +406,6 @@ constexpr int kQB = 32;                   // query rows per streamed step
 // 16 different 16-byte bank groups.
 __device__ __forceinline__ int tswz(int d) { return (d >> 2) & 3; }
 
-// MFMA operand from a transposed block: row d (one column of the tile),
-// 16-byte chunk `chunk` (8 stored rows).
-__device__ __forceinline__ bf16x8 t_op(const unsigned char* t, int d, int chunk) {
-    return as_bf16x8(*reinterpret_cast<const uint4*>(t + d * 64 + ((chunk ^ tswz(d)) << 4)));
-}
-
 // Stage `ROWS` rows (from r_first) of a [rows, D] bf16 slice, row-swizzled as
 // dma_tile does, spread over NW waves.
 template <int D, int ROWS, int NW>

@@ -69,8 +69,6 @@ __device__ __forceinline__ uint4 ld_global16(const uint16_t* p) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
-
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format).
 constexpr int kRsrcWord3 = 0x00020000;
 // Lazy-rescale threshold for the reference maximum, log2 units.
