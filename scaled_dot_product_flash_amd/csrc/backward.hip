@@ -17,17 +17,18 @@
 // Two kernels run in order on the caller's stream:
 //  * bwd_dq_kernel, one workgroup per (batch, query head, 128 query rows),
 //    four waves of 32 rows. It forms Delta and lse * log2(e) for its rows
-//    (stored for the second kernel), keeps its Q and dO rows in registers and
-//    also writes them transposed to the workspace, then streams 64-key tiles
+//    (stored for the second kernel), keeps its Q and dO rows in registers,
+//    then streams 64-key tiles
 //    of K and V through LDS as the forward pass does: S^T = K Q^T and
 //    dP^T = V dO^T on MFMA (a lane owns one query), then dS, then
 //    dQ^T += K^T dS^T with the K^T operand read by the transposing LDS read.
 //  * bwd_dkdv_kernel, one workgroup per (batch, kv head, 256 keys), eight
 //    waves of 32 keys (a lane owns one key). K rows stay in registers and the
-//    workgroup's V rows in LDS; it streams 32-row steps of Q, dO, their
-//    transposed copies, lse and Delta for every query head of the group:
-//    S = Q K^T and dP = dO V^T, P, dS, then dV^T += dO^T P and dK^T += Q^T dS.
-//    Every MFMA operand is a plain 16-byte LDS read. Summing the group's
+//    workgroup's V rows in LDS; it streams 32-row steps of Q, dO, lse and
+//    Delta for every query head of the group: S = Q K^T and dP = dO V^T
+//    (row operands, 16-byte LDS reads), P, dS, then dV^T += dO^T P and
+//    dK^T += Q^T dS with the dO^T and Q^T operands read from the same rows by
+//    the transposing LDS read. Summing the group's
 //    heads inside one workgroup makes dK and dV plain stores, with no atomics.
 //
 // Both kernels take the 32x32x16 bf16 MFMA. Tiles are staged by buffer->LDS
@@ -189,10 +190,9 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2)
 void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
-                   float* __restrict__ Delta, float* __restrict__ L2, uint16_t* __restrict__ dQ,
-                   uint16_t* __restrict__ QT,
-                   uint16_t* __restrict__ dOT, int Hq, int Hkv, int Sq, int Sk, float scale, float c2, int causal,
-                   int window, int nqt, int nitems, int chunk, int pair, int nqb) {
+                   float* __restrict__ Delta, float* __restrict__ L2, uint16_t* __restrict__ dQ, int Hq, int Hkv,
+                   int Sq, int Sk, float scale, float c2, int causal, int window, int nqt, int nitems, int chunk,
+                   int pair) {
     constexpr int BN = kTile, KB = BN / 32, DS = D / 16, DB = D / 32;
     constexpr int TILE_BYTES = BN * D * 2;
     __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILE_BYTES];
@@ -263,34 +263,6 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
             for (int e = 0; e < 8; ++e) dsum = fmaf((float)doreg[s][e], (float)ob[e], dsum);
         }
     }
-    // Transposed copies of this wave's 32 rows of Q and dO for the dK/dV
-    // kernel: one [D][32] bf16 block per (batch, head, 32-row block), the rows
-    // of each 16-row group stored in the order 0-3, 8-11, 4-7, 12-15, the
-    // order in which a 32x32 accumulator hands a lane its rows, so that a
-    // lane there reads its 8 operand values as one 16-byte chunk. The rows go
-    // through this wave's 8 KiB of the first K/V tile buffers and come back
-    // transposed by the transposing LDS read.
-    if (wave_rows) {
-        unsigned char* scr = (wave < 2 ? k_lds0 : k_lds1) + (wave & 1) * (32 * D * 2);
-        const size_t blk = (((size_t)b * Hq + h) * nqb + (wr0 >> 5)) * (size_t)(32 * D);
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            uint16_t* dst = (m == 0 ? QT : dOT) + blk;
-#pragma unroll
-            for (int st = 0; st < DS; ++st)
-                *reinterpret_cast<uint4*>(scr + ln * (D * 2) + (((2 * st + hh) ^ swz<D>(ln)) << 4)) =
-                    __builtin_bit_cast(uint4, m == 0 ? qreg[st] : doreg[st]);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    *reinterpret_cast<uint4*>(dst + (32 * db + ln) * 32 + 16 * c + 8 * hh) =
-                        __builtin_bit_cast(uint4, tr_op<D>(scr, 16 * c, db, lane));
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        }
-    }
-    __syncthreads();  // the scratch is reused by the first K/V tile
 
     const float delta = dsum + __shfl_xor(dsum, 32);
     const size_t row_idx = ((size_t)b * Hq + h) * Sq + qrow;
@@ -401,11 +373,6 @@ constexpr int kKvWaves = 8;               // waves per dK/dV workgroup
 constexpr int kKvKeys = 32 * kKvWaves;    // keys per dK/dV workgroup
 constexpr int kQB = 32;                   // query rows per streamed step
 
-// Chunk swizzle of a transposed [D][32] block in LDS: rows of 64 bytes, four
-// to a 256-byte bank line; 16 lanes reading rows d .. d+15 at one chunk hit
-// 16 different 16-byte bank groups.
-__device__ __forceinline__ int tswz(int d) { return (d >> 2) & 3; }
-
 // Stage `ROWS` rows (from r_first) of a [rows, D] bf16 slice, row-swizzled as
 // dma_tile does, spread over NW waves.
 template <int D, int ROWS, int NW>
@@ -424,27 +391,12 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, int r_first,
     }
 }
 
-// Stage one transposed [D][32] block (D * 64 contiguous bytes from byte
-// offset `src`) with the tswz chunk swizzle.
-template <int D, int NW>
-__device__ __forceinline__ void dma_tblock(__amdgpu_buffer_rsrc_t rs, unsigned src, unsigned char* dst, int wave,
-                                           int lane) {
-    constexpr int SLOTS = D * 64 / 1024;
-    static_assert(SLOTS <= NW, "one DMA slot per wave at most");
-    if (wave < SLOTS) {
-        const int row = 16 * wave + (lane >> 2);
-        const int chunk = (lane & 3) ^ tswz(row);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + wave * 1024), 16,
-                                                 src + (unsigned)(row * 64 + chunk * 16), 0, 0, 0);
-    }
-}
-
 // One workgroup per (batch, kv head, 256 keys), eight waves of 32 keys. A
 // lane owns one key: its K row is the register B operand of S = Q K^T and its
 // V row, read from the workgroup's V block in LDS, that of dP = dO V^T. Each
 // step streams 32 query rows of one query head: Q and dO rows (row operands
-// of S and dP), their transposed blocks (operands of dV^T += dO^T P and
-// dK^T += Q^T dS, plain 16-byte reads), lse (log2 units) and Delta.
+// of S and dP; through the transposing read, the operands of dV^T += dO^T P
+// and dK^T += Q^T dS), lse (log2 units) and Delta.
 //
 // Steps walk the query tiles from the last one down, all heads of the group
 // per tile, so the workgroups of one (batch, kv head) that run together read
@@ -463,21 +415,16 @@ template <int D>
 __global__ __launch_bounds__(64 * kKvWaves, 1)
 void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                     const uint16_t* __restrict__ QT, const uint16_t* __restrict__ dOT,
                      const float* __restrict__ L2, const float* __restrict__ Delta, uint16_t* __restrict__ dK,
                      uint16_t* __restrict__ dV, int Hq, int Hkv, int Sq, int Sk, float scale, float c2, int causal,
-                     int window, int nqb, int nbg, int nsplit, float* __restrict__ part) {
+                     int window, int nbg, int nsplit, float* __restrict__ part) {
     constexpr int NW = kKvWaves, DS = D / 16, DB = D / 32, NP = 2 * DB;
-    constexpr int RT = kQB * D * 2;   // bytes of a row tile and of a transposed block
+    constexpr int RT = kQB * D * 2;   // bytes of a row tile
     __shared__ __attribute__((aligned(16))) unsigned char v_lds[kKvKeys * D * 2];
     __shared__ __attribute__((aligned(16))) unsigned char q_lds0[RT];
     __shared__ __attribute__((aligned(16))) unsigned char q_lds1[RT];
     __shared__ __attribute__((aligned(16))) unsigned char o_lds0[RT];    // dO rows
     __shared__ __attribute__((aligned(16))) unsigned char o_lds1[RT];
-    __shared__ __attribute__((aligned(16))) unsigned char qt_lds0[RT];   // Q^T blocks
-    __shared__ __attribute__((aligned(16))) unsigned char qt_lds1[RT];
-    __shared__ __attribute__((aligned(16))) unsigned char ot_lds0[RT];   // dO^T blocks
-    __shared__ __attribute__((aligned(16))) unsigned char ot_lds1[RT];
     __shared__ __attribute__((aligned(16))) float l_lds0[64];            // lse, log2 units (32 used)
     __shared__ __attribute__((aligned(16))) float l_lds1[64];
     __shared__ __attribute__((aligned(16))) float d_lds0[64];            // Delta
@@ -535,16 +482,12 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         }
 
     // step s: query tile t_hi - s / G of query head g * G + s % G
-    auto issue = [&](int s, unsigned char* qd, unsigned char* od, float* ld, float* dd, unsigned char* qtd,
-                     unsigned char* otd) __attribute__((always_inline)) {
+    auto issue = [&](int s, unsigned char* qd, unsigned char* od, float* ld, float* dd) __attribute__((always_inline)) {
         const int t = t_hi - s / G;
         const int bh = b * Hq + g * G + s % G;
         const size_t rows = (size_t)bh * Sq;
-        const size_t blocks = (size_t)bh * nqb * (kQB * D);
         dma_rows<D, kQB, NW>(rsrc(Q + rows * D, Sq * D * 2), t * kQB, qd, wave, lane);
         dma_rows<D, kQB, NW>(rsrc(dO + rows * D, Sq * D * 2), t * kQB, od, wave, lane);
-        dma_tblock<D, NW>(rsrc(QT + blocks, nqb * RT), (unsigned)(t * RT), qtd, wave, lane);
-        dma_tblock<D, NW>(rsrc(dOT + blocks, nqb * RT), (unsigned)(t * RT), otd, wave, lane);
         if (wave == NW - 1)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(L2 + rows, Sq * 4), (lds_void*)ld, 4,
                                                      (unsigned)((t * kQB + lane) * 4), 0, 0, 0);
@@ -566,8 +509,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     // LDS addresses: with 2st + hh = 2st ^ hh, chunk (2st + hh) ^ sw of a row
     // is chunk hh ^ sw XOR 2st, so the byte offset of k step st is a per-lane
     // base XOR (st << 5) and a tile's base is the instruction's immediate
-    // offset; row 32 d + ln of a transposed block is 2048 d bytes past row
-    // ln. The bases are made opaque at each use so the compiler recomputes
+    // offset. The bases are made opaque at each use so the compiler recomputes
     // the XORs instead of keeping one address register per k step.
     const int sw = swz<D>(ln) ^ hh;
     auto ld16 = [](const unsigned char* p) __attribute__((always_inline)) {
@@ -654,20 +596,17 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
     // dV^T += dO^T P, dK^T += Q^T dS; k step c covers the step's rows
     // 16c .. 16c+15; operands one (c, d) pair ahead
-    auto backward_part = [&](const bf16x8* pb, const bf16x8* dsb, const unsigned char* qtb, const unsigned char* otb)
+    auto backward_part = [&](const bf16x8* pb, const bf16x8* dsb, const unsigned char* qb, const unsigned char* ob)
         __attribute__((always_inline)) {
-        int at = ln * 64 + ((((ln >> 2) & 3) ^ hh) << 4);
-        asm volatile("" : "+v"(at));
-        bf16x8 to = ld16(otb + at), tq = ld16(qtb + at);
+        bf16x8 to = tr_op<D>(ob, 0, 0, lane), tq = tr_op<D>(qb, 0, 0, lane);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int x = 0; x < NP; ++x) {
             const int c = x / DB, d = x % DB;
             bf16x8 no = to, nq = tq;
             if (x + 1 < NP) {
-                const int a = (at ^ (((x + 1) / DB) << 5)) + 2048 * ((x + 1) % DB);
-                no = ld16(otb + a);
-                nq = ld16(qtb + a);
+                no = tr_op<D>(ob, 16 * ((x + 1) / DB), (x + 1) % DB, lane);
+                nq = tr_op<D>(qb, 16 * ((x + 1) / DB), (x + 1) % DB, lane);
             }
             dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to, pb[c], dv[d], 0, 0, 0);
             dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq, dsb[c], dk[d], 0, 0, 0);
@@ -683,14 +622,13 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     auto step = [&](int s, auto r2) __attribute__((always_inline)) {
         constexpr int R = decltype(r2)::value;
         if (s + 1 < s_end)
-            issue(s + 1, R ? q_lds0 : q_lds1, R ? o_lds0 : o_lds1, R ? l_lds0 : l_lds1, R ? d_lds0 : d_lds1,
-                  R ? qt_lds0 : qt_lds1, R ? ot_lds0 : ot_lds1);
+            issue(s + 1, R ? q_lds0 : q_lds1, R ? o_lds0 : o_lds1, R ? l_lds0 : l_lds1, R ? d_lds0 : d_lds1);
         bool edge;
         if (visible_step(s, edge)) {
             bf16x8 pb[2], dsb[2];
             forward_part(R ? q_lds1 : q_lds0, R ? o_lds1 : o_lds0, R ? l_lds1 : l_lds0, R ? d_lds1 : d_lds0,
                          (t_hi - s / G) * kQB, edge, pb, dsb);
-            backward_part(pb, dsb, R ? qt_lds1 : qt_lds0, R ? ot_lds1 : ot_lds0);
+            backward_part(pb, dsb, R ? q_lds1 : q_lds0, R ? o_lds1 : o_lds0);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -699,7 +637,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     if (s_end > s_begin) {
         // the workgroup's V rows stay in LDS for the whole kernel
         dma_rows<D, kKvKeys, NW>(rsrc(V + kv_base, Sk * D * 2), k0, v_lds, wave, lane);
-        issue(s_begin, q_lds0, o_lds0, l_lds0, d_lds0, qt_lds0, ot_lds0);
+        issue(s_begin, q_lds0, o_lds0, l_lds0, d_lds0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         for (int s = s_begin; s < s_end; s += 2) {
@@ -799,15 +737,11 @@ template <int D>
 hipError_t launch_d(const BackwardArgs& a, hipStream_t stream) {
     const float c2 = a.scale * kLog2e;
     // workspace: Delta and lse in log2 units, each [B, Hq, Sq] float32, then
-    // the transposed Q and dO blocks, each [B, Hq, ceil(Sq / 32), D, 32] bf16
-    const int nqb = (a.Sq + kQB - 1) / kQB;
+    // the split partials of dK and dV (several runs per key block only)
     unsigned char* ws = static_cast<unsigned char*>(a.ws);
     const size_t rbytes = align256((size_t)a.B * a.Hq * a.Sq * 4);
     float* delta = reinterpret_cast<float*>(ws);
     float* l2 = reinterpret_cast<float*>(ws + rbytes);
-    const size_t tbytes = (size_t)a.B * a.Hq * nqb * kQB * D * 2;
-    uint16_t* qt = reinterpret_cast<uint16_t*>(ws + 2 * rbytes);
-    uint16_t* dot = reinterpret_cast<uint16_t*>(reinterpret_cast<unsigned char*>(qt) + align256(tbytes));
     if (a.Sq > 0) {
         const int nqt = (a.Sq + kRows - 1) / kRows;
         const long long nitems = (long long)a.B * a.Hq * nqt;
@@ -823,16 +757,15 @@ hipError_t launch_d(const BackwardArgs& a, hipStream_t stream) {
                          a.causal, a.window, grid, kThreads, nitems, kRows, deal.chunk, pair);
         hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.o,
-                           (const uint16_t*)a.dout, a.lse, delta, l2, (uint16_t*)a.dq, qt, dot, a.Hq, a.Hkv, a.Sq, a.Sk,
-                           a.scale, c2, a.causal, a.window, nqt, (int)nitems, (int)deal.chunk, pair, nqb);
+                           (const uint16_t*)a.dout, a.lse, delta, l2, (uint16_t*)a.dq, a.Hq, a.Hkv, a.Sq, a.Sk,
+                           a.scale, c2, a.causal, a.window, nqt, (int)nitems, (int)deal.chunk, pair);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int nkt = (a.Sk + kKvKeys - 1) / kKvKeys;
     const int nbg = a.B * a.Hkv;
     const int nsplit = a.Sq > 0 ? a.kv_splits : 1;
-    float* part = nsplit > 1 ? reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(dot) + align256(tbytes))
-                             : nullptr;
+    float* part = nsplit > 1 ? reinterpret_cast<float*>(ws + 2 * rbytes) : nullptr;
     const long long grid = (long long)nbg * nkt * nsplit;
     if (!grid_fits(grid, 64 * kKvWaves)) return hipErrorInvalidValue;
     if (log_enabled())
@@ -841,8 +774,8 @@ hipError_t launch_d(const BackwardArgs& a, hipStream_t stream) {
                      nsplit > 1 ? " + bwd_kv_reduce_kernel" : "");
     hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)grid), dim3(64 * kKvWaves), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
-                       qt, dot, l2, delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.Hq, a.Hkv, a.Sq, a.Sk, a.scale, c2,
-                       a.causal, a.window, nqb, nbg, nsplit, part);
+                       l2, delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.Hq, a.Hkv, a.Sq, a.Sk, a.scale, c2,
+                       a.causal, a.window, nbg, nsplit, part);
     if (nsplit > 1) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -868,8 +801,8 @@ int backward_kv_splits(int B, int Hkv, int Sq, int Sk, int num_cu) {
 }
 
 size_t backward_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, int kv_splits) {
-    const size_t nqb = (size_t)(Sq + kQB - 1) / kQB;
-    size_t bytes = 2 * align256((size_t)B * Hq * Sq * 4) + 2 * align256((size_t)B * Hq * nqb * kQB * D * 2);
+    (void)D;
+    size_t bytes = 2 * align256((size_t)B * Hq * Sq * 4);
     if (kv_splits > 1) bytes += 2 * (size_t)kv_splits * B * Hkv * Sk * D * 4;
     return bytes;
 }
