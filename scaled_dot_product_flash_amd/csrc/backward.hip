@@ -22,8 +22,10 @@
 //    of K and V through LDS as the forward pass does: S^T = K Q^T and
 //    dP^T = V dO^T on MFMA (a lane owns one query), then dS, then
 //    dQ^T += K^T dS^T with the K^T operand read by the transposing LDS read.
-//  * bwd_dkdv_kernel, one workgroup per (batch, kv head, 256 keys), eight
-//    waves of 32 keys (a lane owns one key). K rows stay in registers and the
+//  * bwd_dkdv_kernel, one workgroup per (batch, kv head, 128 keys), four
+//    waves of 32 keys (a lane owns one key), two workgroups per CU whose
+//    barriers do not couple, so the two waves of a SIMD drift out of phase
+//    and one's softmax runs beside the other's MFMAs. K rows stay in registers and the
 //    workgroup's V rows in LDS; it streams 32-row steps of Q, dO, lse and
 //    Delta for every query head of the group: S = Q K^T and dP = dO V^T
 //    (row operands, 16-byte LDS reads), P, dS, then dV^T += dO^T P and
@@ -369,7 +371,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // dK, dV
 
-constexpr int kKvWaves = 8;               // waves per dK/dV workgroup
+constexpr int kKvWaves = 4;               // waves per dK/dV workgroup
 constexpr int kKvKeys = 32 * kKvWaves;    // keys per dK/dV workgroup
 constexpr int kQB = 32;                   // query rows per streamed step
 
@@ -391,7 +393,7 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, int r_first,
     }
 }
 
-// One workgroup per (batch, kv head, 256 keys), eight waves of 32 keys. A
+// One workgroup per (batch, kv head, 128 keys), four waves of 32 keys. A
 // lane owns one key: its K row is the register B operand of S = Q K^T and its
 // V row, read from the workgroup's V block in LDS, that of dP = dO V^T. Each
 // step streams 32 query rows of one query head: Q and dO rows (row operands
@@ -412,7 +414,7 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, int r_first,
 // bwd_kv_reduce_kernel sums in split order into the bf16 outputs. With one
 // run the kernel writes dK and dV itself.
 template <int D>
-__global__ __launch_bounds__(64 * kKvWaves, 1)
+__global__ __launch_bounds__(64 * kKvWaves, 2)
 void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                      const float* __restrict__ L2, const float* __restrict__ Delta, uint16_t* __restrict__ dK,
