@@ -99,6 +99,17 @@ def test_prefill_validation(lib, kwargs, code, f32):
 
 
 @pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_longest_key_range_boundary(lib, D, f32):
+    # the longest key range with Sk * D * 4 < 2^31 passes validation (the call
+    # then stops at the HIP runtime, there being no GPU here); one key more is
+    # a size error. tests/test_gpu_max_sizes.py runs the longest range.
+    sk = (2 ** 31 - 1) // (D * 4)
+    assert _fwd(lib, D=D, Sk=sk + 1, f32=f32) == SHAPE
+    assert _fwd(lib, D=D, Sk=sk, f32=f32) == HIP
+
+
+@pytest.mark.parametrize("f32", [False, True])
 def test_prefill_empty_calls_are_no_ops(lib, f32):
     # nothing to compute: no pointer is needed and no HIP call is made
     assert _fwd(lib, q=None, k=None, v=None, o=None, B=0, f32=f32) == OK
