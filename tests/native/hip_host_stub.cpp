@@ -4,14 +4,19 @@
 // address sanitizer sees every workspace access the host code makes),
 // kernel launches are recorded and checked against the launch limits of the
 // hardware instead of being run, and stream capture can be switched on to
-// reach the capture error path. Nothing here touches a GPU.
+// reach the capture error path. Nothing here touches a GPU. It is
+// thread-safe, so the library's own locking can be checked under the thread
+// sanitizer: the launch configuration is per thread, the counters and
+// switches are atomic, and the stand-in memory of device symbols is locked.
 
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 
 namespace {
@@ -21,7 +26,7 @@ struct Config {
     size_t shmem;
     hipStream_t stream;
 };
-Config g_cfg;
+thread_local Config g_cfg;
 // function-local: the library's registration constructors run before this
 // file's globals would be constructed
 std::map<const void*, std::string>& kernels() {   // host stub -> device name
@@ -36,9 +41,13 @@ std::map<const void*, void*>& var_mem() {         // host shadow -> stand-in dev
     static std::map<const void*, void*> m;
     return m;
 }
-long long g_launches = 0;
-int g_capturing = 0;
-int g_no_device = 0;
+std::mutex& var_mutex() {
+    static std::mutex m;
+    return m;
+}
+std::atomic<long long> g_launches{0};
+std::atomic<int> g_capturing{0};
+std::atomic<int> g_no_device{0};
 
 [[noreturn]] void fail(const char* what, const void* f) {
     auto it = kernels().find(f);
@@ -55,6 +64,7 @@ extern "C" long long stub_launches() { return g_launches; }
 extern "C" void stub_set_capturing(int on) { g_capturing = on; }
 extern "C" void stub_set_no_device(int on) { g_no_device = on; }
 extern "C" void stub_release() {
+    std::lock_guard<std::mutex> lock(var_mutex());
     for (auto& kv : var_mem()) std::free(kv.second);
     var_mem().clear();
 }
@@ -135,6 +145,7 @@ hipError_t hipGetLastError() { return hipSuccess; }
 hipError_t hipGetSymbolAddress(void** p, const void* sym) {
     auto it = vars().find(sym);
     if (it == vars().end()) return hipErrorInvalidSymbol;
+    std::lock_guard<std::mutex> lock(var_mutex());
     void*& mem = var_mem()[sym];
     if (!mem) mem = std::calloc(1, it->second);
     *p = mem;

@@ -1,4 +1,5 @@
-"""The library's host code under the address and undefined-behaviour sanitizers.
+"""The library's host code under the address, undefined-behaviour and thread
+sanitizers.
 
 Every host source of libattn.so (the C ABI, the page pool and the launchers
 in the kernel files) is compiled for the host only with ASan and UBSan and
@@ -8,7 +9,10 @@ checks every kernel launch against the hardware's grid limits instead of
 running it. tests/native/abi_host_check.cpp then drives each entry point:
 the documented error codes, a sweep over boundary values of every size and
 mask argument, and the page pool under random resizes. Any sanitizer report
-or launch-limit violation aborts the program. CPU only.
+or launch-limit violation aborts the program. A second build with the thread
+sanitizer runs tests/native/abi_threads_check.cpp: eight threads on four
+streams calling every entry point at once, with workspaces that grow and one
+shared page pool. CPU only.
 """
 
 import os
@@ -33,19 +37,24 @@ def _tool(name, fallback):
     return shutil.which(name) or (fallback if os.path.exists(fallback) else None)
 
 
-@pytest.fixture(scope="module")
-def host_check(tmp_path_factory):
+# thread sanitizer (cannot be combined with the address sanitizer); its
+# host objects come from clang, so the stand-in runtime, the driver and the
+# link use clang too, for one sanitizer runtime throughout
+HOST_TSAN = ["-Xarch_host", "-fsanitize=thread"]
+CXX_TSAN = ["-fsanitize=thread"]
+
+
+def _build(d, host_flags, cxx_name, cxx_fallback, cxx_flags, driver, extra_link=()):
     hipcc = _tool("hipcc", "/opt/rocm/bin/hipcc")
-    gxx = _tool("g++", "/usr/bin/g++")
+    gxx = _tool(cxx_name, cxx_fallback)
     if hipcc is None or gxx is None:
-        pytest.skip("hipcc and g++ are needed")
-    d = tmp_path_factory.mktemp("host_san")
+        pytest.skip(f"hipcc and {cxx_name} are needed")
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     objs, procs = [], []
     for src in SOURCES:
         obj = str(d / (src + ".o"))
         cmd = [hipcc, "-x", "hip", "--cuda-host-only", "--offload-arch=gfx950", "-O1", "-g", "-std=c++17",
-               "-fPIC", "-fno-omit-frame-pointer", *HOST_SAN, *inc, "-c", os.path.join(CSRC, src), "-o", obj]
+               "-fPIC", "-fno-omit-frame-pointer", *host_flags, *inc, "-c", os.path.join(CSRC, src), "-o", obj]
         procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
         objs.append(obj)
     for p, src in zip(procs, SOURCES):
@@ -57,16 +66,27 @@ def host_check(tmp_path_factory):
     fatbins = sorted(set(re.findall(r"\b(__hip_fatbin_\w+)", nm)))
     defs = d / "fatbins.c"
     defs.write_text("".join(f"char {n}[64];\n" for n in fatbins))
-    exe = str(d / "abi_host_check")
-    for src in ("hip_host_stub.cpp", "abi_host_check.cpp"):
-        subprocess.run([gxx, "-O1", "-g", "-std=c++17", "-fno-omit-frame-pointer", *GXX_SAN, "-D__HIP_PLATFORM_AMD__",
+    exe = str(d / driver.replace(".cpp", ""))
+    for src in ("hip_host_stub.cpp", driver):
+        subprocess.run([gxx, "-O1", "-g", "-std=c++17", "-fno-omit-frame-pointer", *cxx_flags, "-D__HIP_PLATFORM_AMD__",
                         "-I", "/opt/rocm/include", *inc, "-c", os.path.join(NATIVE, src), "-o",
                         str(d / (src + ".o"))], check=True, capture_output=True, text=True, timeout=300)
-    subprocess.run([gxx, "-c", str(defs), "-o", str(d / "fatbins.o")], check=True, timeout=60)
-    subprocess.run([gxx, *GXX_SAN, "-o", exe, *objs, str(d / "hip_host_stub.cpp.o"),
-                    str(d / "abi_host_check.cpp.o"), str(d / "fatbins.o")],
+    subprocess.run([gxx, "-x", "c", "-c", str(defs), "-o", str(d / "fatbins.o")], check=True, timeout=60)
+    subprocess.run([gxx, *cxx_flags, "-o", exe, *objs, str(d / "hip_host_stub.cpp.o"),
+                    str(d / (driver + ".o")), str(d / "fatbins.o"), *extra_link],
                    check=True, capture_output=True, text=True, timeout=300)
     return exe
+
+
+@pytest.fixture(scope="module")
+def host_check(tmp_path_factory):
+    return _build(tmp_path_factory.mktemp("host_san"), HOST_SAN, "g++", "/usr/bin/g++", GXX_SAN, "abi_host_check.cpp")
+
+
+@pytest.fixture(scope="module")
+def threads_check(tmp_path_factory):
+    return _build(tmp_path_factory.mktemp("host_tsan"), HOST_TSAN, "/opt/rocm/llvm/bin/clang++",
+                  "/opt/rocm/llvm/bin/clang++", CXX_TSAN, "abi_threads_check.cpp", ("-pthread",))
 
 
 def test_host_code_under_sanitizers(host_check):
@@ -105,3 +125,12 @@ def test_dispatch_log(host_check):
     env.pop("ATTN_LOG")
     quiet = subprocess.run([host_check, "0"], capture_output=True, text=True, timeout=600, env=env)
     assert quiet.returncode == 0 and "[attn]" not in quiet.stderr
+
+
+def test_host_code_under_thread_sanitizer(threads_check):
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1:second_deadlock_stack=1")
+    run = subprocess.run([threads_check, "200"], capture_output=True, text=True, timeout=600, env=env)
+    assert run.returncode == 0, (run.stdout[-3000:], run.stderr[-6000:])
+    assert "ThreadSanitizer" not in run.stderr, run.stderr[-6000:]
+    assert run.stdout.strip().startswith("thread checks ok")
+    assert int(re.search(r"launches (\d+)", run.stdout).group(1)) > 8 * 200 * 9
