@@ -22,7 +22,8 @@
 //    of K and V through LDS as the forward pass does: S^T = K Q^T and
 //    dP^T = V dO^T on MFMA (a lane owns one query), then dS, then
 //    dQ^T += K^T dS^T with the K^T operand read by the transposing LDS read.
-//  * bwd_dkdv_kernel, one workgroup per (batch, kv head, 128 keys), four
+//  * bwd_dkdv_kernel, one workgroup per (batch, kv head, 128 keys) (under a
+//    causal mask, per pair of such key blocks), four
 //    waves of 32 keys (a lane owns one key), two workgroups per CU whose
 //    barriers do not couple, so the two waves of a SIMD drift out of phase
 //    and one's softmax runs beside the other's MFMAs. K rows stay in registers and the
@@ -400,12 +401,22 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, int r_first,
 // of S and dP; through the transposing read, the operands of dV^T += dO^T P
 // and dK^T += Q^T dS), lse (log2 units) and Delta.
 //
-// Steps walk the query tiles from the last one down, all heads of the group
-// per tile, so the workgroups of one (batch, kv head) that run together read
-// the same tiles at about the same time. Workgroups are dispatched key block
-// major: under a causal mask the first key blocks carry the most work and go
-// first, and with (batch, kv head) = blockIdx % (B * Hkv) one (batch, kv head)
-// stays on one XCD when B * Hkv is a multiple of 8.
+// A step covers one query tile of one head, all heads of the group per tile.
+// Under a causal mask key block kt sees the query tiles from about its own
+// position to the last, so its work falls with kt. There (with no window and
+// one run per key block) workgroup pi takes two key blocks: first nkt-1-pi,
+// walking its tiles from the last one down, then pi, walking its tiles from
+// the first one up. Every workgroup then does the same work (the two
+// blocks' tile counts add up to a constant) in a single round, and at every
+// moment all workgroups of one (batch, kv head) are on the same tile in each
+// phase, the first-phase ones at tile T - tau, the second-phase ones at tile
+// tau - c for the same step count tau, so each tile comes from HBM about once
+// per phase (the dK/dV kernel fetches 1.5x its algorithmic bytes at the 4k
+// shape, 4.4x with one key block per workgroup, whose second round of blocks
+// re-read the tiles staggered). Otherwise workgroup w takes key block
+// w / (B * Hkv * nsplit), walking its tiles from the last one down. With
+// (batch, kv head) = blockIdx % (B * Hkv), one (batch, kv head) stays on one
+// XCD when B * Hkv is a multiple of 8.
 //
 // When the key blocks are too few to fill the chip (MQA, a single sequence),
 // each key block's steps are cut into `nsplit` contiguous runs, one workgroup
@@ -419,7 +430,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                      const float* __restrict__ L2, const float* __restrict__ Delta, uint16_t* __restrict__ dK,
                      uint16_t* __restrict__ dV, int Hq, int Hkv, int Sq, int Sk, float scale, float c2, int causal,
-                     int window, int nbg, int nsplit, float* __restrict__ part) {
+                     int window, int nbg, int nsplit, float* __restrict__ part, int nkt, int paired) {
     constexpr int NW = kKvWaves, DS = D / 16, DB = D / 32, NP = 2 * DB;
     constexpr int RT = kQB * D * 2;   // bytes of a row tile
     __shared__ __attribute__((aligned(16))) unsigned char v_lds[kKvKeys * D * 2];
@@ -433,9 +444,14 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     __shared__ __attribute__((aligned(16))) float d_lds1[64];
 
     const int w = blockIdx.x;
-    const int kt = w / (nbg * nsplit);
-    const int split = (w / nbg) % nsplit;
+    const int split = paired ? 0 : (w / nbg) % nsplit;
     const int bg = w % nbg;
+    // paired: key block nkt - 1 - pi walking the query tiles top-down, then
+    // key block pi walking them bottom-up (one block for the middle of an
+    // odd count)
+    const int pi = w / nbg;
+    const int kt_first = paired ? nkt - 1 - pi : w / (nbg * nsplit);
+    const int nblk = paired && pi != nkt - 1 - pi ? 2 : 1;
     const int G = Hq / Hkv;
     const int g = bg % Hkv;
     const int b = bg / Hkv;
@@ -447,272 +463,288 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const int hh = lane >> 5;
 
     const int off = Sk - Sq;
-    const int k0 = kt * kKvKeys;
-    const int kw0 = k0 + 32 * wave;                 // first key of this wave
-    const int kw1 = min(kw0 + 31, Sk - 1);
-    const bool wave_keys = kw0 < Sk;
-    const int key = kw0 + ln;
-    const bool key_ok = key < Sk;
+    auto run_block = [&](int kt, bool down) __attribute__((always_inline)) {
+        const int k0 = kt * kKvKeys;
+        const int kw0 = k0 + 32 * wave;                 // first key of this wave
+        const int kw1 = min(kw0 + 31, Sk - 1);
+        const bool wave_keys = kw0 < Sk;
+        const int key = kw0 + ln;
+        const bool key_ok = key < Sk;
 
-    const size_t kv_base = ((size_t)b * Hkv + g) * (size_t)Sk * D;
-    bf16x8 kreg[DS];
-    {
-        const size_t rb = kv_base + (size_t)(key_ok ? key : 0) * D + 8 * hh;
+        const size_t kv_base = ((size_t)b * Hkv + g) * (size_t)Sk * D;
+        bf16x8 kreg[DS];
+        {
+            const size_t rb = kv_base + (size_t)(key_ok ? key : 0) * D + 8 * hh;
 #pragma unroll
-        for (int s = 0; s < DS; ++s) kreg[s] = as_bf16x8(key_ok ? ld_global16(K + rb + 16 * s) : make_uint4(0, 0, 0, 0));
-    }
-
-    // queries that see at least one key of the workgroup: position p = q + off
-    // sees key j iff j <= p (causal) and j > p - window
-    const int kmax = min(k0 + kKvKeys, Sk) - 1;
-    const int q_lo = causal ? max(0, k0 - off) : 0;
-    const int q_hi = (causal && window > 0) ? min(Sq - 1, kmax + window - 1 - off) : Sq - 1;
-    const int t_hi = q_hi / kQB;
-    const int nt = q_lo <= q_hi ? t_hi - q_lo / kQB + 1 : 0;
-    const int nsteps = G * nt;
-    // this workgroup's run of steps
-    const int s_begin = (int)((long long)nsteps * split / nsplit);
-    const int s_end = (int)((long long)nsteps * (split + 1) / nsplit);
-
-    f32x16 dk[DB], dv[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            dk[db][v] = 0.f;
-            dv[db][v] = 0.f;
+            for (int s = 0; s < DS; ++s)
+                kreg[s] = as_bf16x8(key_ok ? ld_global16(K + rb + 16 * s) : make_uint4(0, 0, 0, 0));
         }
 
-    // step s: query tile t_hi - s / G of query head g * G + s % G
-    auto issue = [&](int s, unsigned char* qd, unsigned char* od, float* ld, float* dd) __attribute__((always_inline)) {
-        const int t = t_hi - s / G;
-        const int bh = b * Hq + g * G + s % G;
-        const size_t rows = (size_t)bh * Sq;
-        dma_rows<D, kQB, NW>(rsrc(Q + rows * D, Sq * D * 2), t * kQB, qd, wave, lane);
-        dma_rows<D, kQB, NW>(rsrc(dO + rows * D, Sq * D * 2), t * kQB, od, wave, lane);
-        if (wave == NW - 1)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(L2 + rows, Sq * 4), (lds_void*)ld, 4,
-                                                     (unsigned)((t * kQB + lane) * 4), 0, 0, 0);
-        else if (wave == NW - 2)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(Delta + rows, Sq * 4), (lds_void*)dd, 4,
-                                                     (unsigned)((t * kQB + lane) * 4), 0, 0, 0);
-    };
-    // does step s have a visible (query, key) pair for this wave; does it
-    // need the mask (a boundary or a tail crosses it)
-    auto visible_step = [&](int s, bool& edge) __attribute__((always_inline)) {
-        const int qa = (t_hi - s / G) * kQB;
-        const int pa = qa + off, pe = min(qa + kQB - 1, Sq - 1) + off;
-        const bool any = wave_keys && (!causal || kw0 <= pe) && (window == 0 || kw1 > pa - window);
-        edge = !((qa + kQB - 1 < Sq) && (kw0 + 31 < Sk) && (!causal || kw0 + 31 <= pa) &&
-                 (window == 0 || kw0 > pe - window));
-        return any;
-    };
+        // queries that see at least one key of the workgroup: position p = q + off
+        // sees key j iff j <= p (causal) and j > p - window
+        const int kmax = min(k0 + kKvKeys, Sk) - 1;
+        const int q_lo = causal ? max(0, k0 - off) : 0;
+        const int q_hi = (causal && window > 0) ? min(Sq - 1, kmax + window - 1 - off) : Sq - 1;
+        const int t_hi = q_hi / kQB;
+        const int t_lo = q_lo / kQB;
+        const int nt = q_lo <= q_hi ? t_hi - t_lo + 1 : 0;
+        // query tile of step s
+        auto tile_of = [&](int s) __attribute__((always_inline)) { return down ? t_hi - s / G : t_lo + s / G; };
+        const int nsteps = G * nt;
+        // this workgroup's run of steps
+        const int s_begin = (int)((long long)nsteps * split / nsplit);
+        const int s_end = (int)((long long)nsteps * (split + 1) / nsplit);
 
-    // LDS addresses: with 2st + hh = 2st ^ hh, chunk (2st + hh) ^ sw of a row
-    // is chunk hh ^ sw XOR 2st, so the byte offset of k step st is a per-lane
-    // base XOR (st << 5) and a tile's base is the instruction's immediate
-    // offset. The bases are made opaque at each use so the compiler recomputes
-    // the XORs instead of keeping one address register per k step.
-    const int sw = swz<D>(ln) ^ hh;
-    auto ld16 = [](const unsigned char* p) __attribute__((always_inline)) {
-        return as_bf16x8(*reinterpret_cast<const uint4*>(p));
-    };
-
-    // S and dP of one step, then P and dS packed as bf16 operands. Operands
-    // are read one k step ahead of their MFMAs, and the scheduling barriers
-    // keep the compiler from hoisting more reads than that (the register file
-    // holds K, dK and dV for the whole kernel).
-    auto forward_part = [&](const unsigned char* qb, const unsigned char* ob, const float* lb, const float* dlb,
-                            int qa, bool edge, bf16x8* pb, bf16x8* dsb) __attribute__((always_inline)) {
-        int aq = ln * (D * 2) + (sw << 4);
-        int av = (32 * wave + ln) * (D * 2) + (sw << 4);
-        asm volatile("" : "+v"(aq), "+v"(av));
-        f32x16 S, P;
+        f32x16 dk[DB], dv[DB];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            S[v] = 0.f;
-            P[v] = 0.f;
-        }
-        bf16x8 aqo = ld16(qb + aq), aoo = ld16(ob + aq), avo = ld16(v_lds + av);
-        // the two waves of a SIMD meet at every barrier and would run their
-        // MFMA and softmax phases side by side; a raised priority while a wave
-        // issues MFMAs lets the first one through its block, so the other's
-        // VALU work overlaps it (about 1.5 % on the dK/dV kernel; in the dQ
-        // kernel, two workgroups per CU and no such lockstep, it costs 2 %)
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int st = 0; st < DS; ++st) {
-            bf16x8 nq = aqo, no = aoo, nv = avo;
-            if (st + 1 < DS) {
-                const int x = (st + 1) << 5;
-                nq = ld16(qb + (aq ^ x));
-                no = ld16(ob + (aq ^ x));
-                nv = ld16(v_lds + (av ^ x));
-            }
-            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqo, kreg[st], S, 0, 0, 0);
-            P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aoo, avo, P, 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            aqo = nq;
-            aoo = no;
-            avo = nv;
-        }
-        __builtin_amdgcn_s_setprio(0);
-        // accumulator value v holds query row 8(v/4) + 4hh + v%4 of the step;
-        // masked pairs get an exponent of -inf, so P = 0 and dS = 0 exactly
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float4 l4 = *reinterpret_cast<const float4*>(lb + 8 * j + 4 * hh);
-            const float l[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[4 * j + i] = fmaf(S[4 * j + i], c2, -l[i]);
-        }
-        if (edge) {
-            asm volatile("");
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int q = qa + 8 * (v >> 2) + 4 * hh + (v & 3);
-                const int p = q + off;
-                bool ok = q < Sq && key_ok;
-                if (causal) ok = ok && key <= p;
-                if (window > 0) ok = ok && key > p - window;
-                S[v] = ok ? S[v] : -INFINITY;
+                dk[db][v] = 0.f;
+                dv[db][v] = 0.f;
             }
-        }
+
+        // step s: query tile t_hi - s / G of query head g * G + s % G
+        auto issue = [&](int s, unsigned char* qd, unsigned char* od, float* ld, float* dd)
+            __attribute__((always_inline)) {
+            const int t = tile_of(s);
+            const int bh = b * Hq + g * G + s % G;
+            const size_t rows = (size_t)bh * Sq;
+            dma_rows<D, kQB, NW>(rsrc(Q + rows * D, Sq * D * 2), t * kQB, qd, wave, lane);
+            dma_rows<D, kQB, NW>(rsrc(dO + rows * D, Sq * D * 2), t * kQB, od, wave, lane);
+            if (wave == NW - 1)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(L2 + rows, Sq * 4), (lds_void*)ld, 4,
+                                                         (unsigned)((t * kQB + lane) * 4), 0, 0, 0);
+            else if (wave == NW - 2)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(Delta + rows, Sq * 4), (lds_void*)dd, 4,
+                                                         (unsigned)((t * kQB + lane) * 4), 0, 0, 0);
+        };
+        // does step s have a visible (query, key) pair for this wave; does it
+        // need the mask (a boundary or a tail crosses it)
+        auto visible_step = [&](int s, bool& edge) __attribute__((always_inline)) {
+            const int qa = tile_of(s) * kQB;
+            const int pa = qa + off, pe = min(qa + kQB - 1, Sq - 1) + off;
+            const bool any = wave_keys && (!causal || kw0 <= pe) && (window == 0 || kw1 > pa - window);
+            edge = !((qa + kQB - 1 < Sq) && (kw0 + 31 < Sk) && (!causal || kw0 + 31 <= pa) &&
+                     (window == 0 || kw0 > pe - window));
+            return any;
+        };
+
+        // LDS addresses: with 2st + hh = 2st ^ hh, chunk (2st + hh) ^ sw of a row
+        // is chunk hh ^ sw XOR 2st, so the byte offset of k step st is a per-lane
+        // base XOR (st << 5) and a tile's base is the instruction's immediate
+        // offset. The bases are made opaque at each use so the compiler recomputes
+        // the XORs instead of keeping one address register per k step.
+        const int sw = swz<D>(ln) ^ hh;
+        auto ld16 = [](const unsigned char* p) __attribute__((always_inline)) {
+            return as_bf16x8(*reinterpret_cast<const uint4*>(p));
+        };
+
+        // S and dP of one step, then P and dS packed as bf16 operands. Operands
+        // are read one k step ahead of their MFMAs, and the scheduling barriers
+        // keep the compiler from hoisting more reads than that (the register file
+        // holds K, dK and dV for the whole kernel).
+        auto forward_part = [&](const unsigned char* qb, const unsigned char* ob, const float* lb, const float* dlb,
+                                int qa, bool edge, bf16x8* pb, bf16x8* dsb) __attribute__((always_inline)) {
+            int aq = ln * (D * 2) + (sw << 4);
+            int av = (32 * wave + ln) * (D * 2) + (sw << 4);
+            asm volatile("" : "+v"(aq), "+v"(av));
+            f32x16 S, P;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float4 d4 = *reinterpret_cast<const float4*>(dlb + 8 * j + 4 * hh);
-            const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int v = 4 * j + i;
-                S[v] = __builtin_amdgcn_exp2f(S[v]);
-                P[v] = S[v] * (P[v] - dl[i]);
+            for (int v = 0; v < 16; ++v) {
+                S[v] = 0.f;
+                P[v] = 0.f;
             }
-        }
-        pb[0] = pack8(S, 0);
-        pb[1] = pack8(S, 1);
-        dsb[0] = pack8(P, 0);
-        dsb[1] = pack8(P, 1);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // dV^T += dO^T P, dK^T += Q^T dS; k step c covers the step's rows
-    // 16c .. 16c+15; operands one (c, d) pair ahead
-    auto backward_part = [&](const bf16x8* pb, const bf16x8* dsb, const unsigned char* qb, const unsigned char* ob)
-        __attribute__((always_inline)) {
-        bf16x8 to = tr_op<D>(ob, 0, 0, lane), tq = tr_op<D>(qb, 0, 0, lane);
-        __builtin_amdgcn_s_setprio(1);
+            bf16x8 aqo = ld16(qb + aq), aoo = ld16(ob + aq), avo = ld16(v_lds + av);
+            // the two waves of a SIMD meet at every barrier and would run their
+            // MFMA and softmax phases side by side; a raised priority while a wave
+            // issues MFMAs lets the first one through its block, so the other's
+            // VALU work overlaps it (about 1.5 % on the dK/dV kernel; in the dQ
+            // kernel, two workgroups per CU and no such lockstep, it costs 2 %)
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int x = 0; x < NP; ++x) {
-            const int c = x / DB, d = x % DB;
-            bf16x8 no = to, nq = tq;
-            if (x + 1 < NP) {
-                no = tr_op<D>(ob, 16 * ((x + 1) / DB), (x + 1) % DB, lane);
-                nq = tr_op<D>(qb, 16 * ((x + 1) / DB), (x + 1) % DB, lane);
+            for (int st = 0; st < DS; ++st) {
+                bf16x8 nq = aqo, no = aoo, nv = avo;
+                if (st + 1 < DS) {
+                    const int x = (st + 1) << 5;
+                    nq = ld16(qb + (aq ^ x));
+                    no = ld16(ob + (aq ^ x));
+                    nv = ld16(v_lds + (av ^ x));
+                }
+                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqo, kreg[st], S, 0, 0, 0);
+                P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aoo, avo, P, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                aqo = nq;
+                aoo = no;
+                avo = nv;
             }
-            dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to, pb[c], dv[d], 0, 0, 0);
-            dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq, dsb[c], dk[d], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            to = no;
-            tq = nq;
-        }
-        __builtin_amdgcn_s_setprio(0);
-    };
-
-    // step s, its tiles in the buffers of parity R (compile-time, so that
-    // every LDS address is a constant offset)
-    auto step = [&](int s, auto r2) __attribute__((always_inline)) {
-        constexpr int R = decltype(r2)::value;
-        if (s + 1 < s_end)
-            issue(s + 1, R ? q_lds0 : q_lds1, R ? o_lds0 : o_lds1, R ? l_lds0 : l_lds1, R ? d_lds0 : d_lds1);
-        bool edge;
-        if (visible_step(s, edge)) {
-            bf16x8 pb[2], dsb[2];
-            forward_part(R ? q_lds1 : q_lds0, R ? o_lds1 : o_lds0, R ? l_lds1 : l_lds0, R ? d_lds1 : d_lds0,
-                         (t_hi - s / G) * kQB, edge, pb, dsb);
-            backward_part(pb, dsb, R ? q_lds1 : q_lds0, R ? o_lds1 : o_lds0);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    };
-
-    if (s_end > s_begin) {
-        // the workgroup's V rows stay in LDS for the whole kernel
-        dma_rows<D, kKvKeys, NW>(rsrc(V + kv_base, Sk * D * 2), k0, v_lds, wave, lane);
-        issue(s_begin, q_lds0, o_lds0, l_lds0, d_lds0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        for (int s = s_begin; s < s_end; s += 2) {
-            step(s, std::integral_constant<int, 0>());
-            if (s + 1 < s_end) step(s + 1, std::integral_constant<int, 1>());
-        }
-    }
-
-    // accumulator value v of block db holds d = 32 db + 8(v/4) + 4hh + v%4
-    if (!wave_keys) return;
-    if (part != nullptr) {
-        const size_t plane = (size_t)nbg * Sk * D;
-        if constexpr (D == 128) {
-            // float partials, 64 columns (two d blocks, 256 bytes of a row)
-            // per pass through the wave's 8 KiB of V rows in LDS, read back
-            // as whole 256-byte row segments, four rows per store instruction
-            unsigned char* stage = v_lds + wave * (32 * D * 2);
-            const int cl = lane & 15;
+            __builtin_amdgcn_s_setprio(0);
+            // accumulator value v holds query row 8(v/4) + 4hh + v%4 of the step;
+            // masked pairs get an exponent of -inf, so P = 0 and dS = 0 exactly
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                float* base = part + (size_t)(m * nsplit + split) * plane + ((size_t)bg * Sk + kw0) * D;
+            for (int j = 0; j < 4; ++j) {
+                const float4 l4 = *reinterpret_cast<const float4*>(lb + 8 * j + 4 * hh);
+                const float l[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-                for (int pass = 0; pass < 2; ++pass) {
+                for (int i = 0; i < 4; ++i) S[4 * j + i] = fmaf(S[4 * j + i], c2, -l[i]);
+            }
+            if (edge) {
+                asm volatile("");
 #pragma unroll
-                    for (int x = 0; x < 2; ++x)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const f32x16& acc = m == 0 ? dk[2 * pass + x] : dv[2 * pass + x];
-                            const float s = m == 0 ? scale : 1.f;
-                            const int chunk = (8 * x + 2 * r + hh) ^ (ln & 15);
-                            *reinterpret_cast<float4*>(stage + ln * 256 + chunk * 16) =
-                                make_float4(acc[4 * r] * s, acc[4 * r + 1] * s, acc[4 * r + 2] * s, acc[4 * r + 3] * s);
-                        }
-                    wave_lds_fence();
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int row = 4 * i + (lane >> 4);
-                        const float4 v4 = *reinterpret_cast<const float4*>(stage + row * 256 + ((cl ^ (row & 15)) << 4));
-                        if (kw0 + row < Sk) *reinterpret_cast<float4*>(base + (size_t)row * D + 64 * pass + 4 * cl) = v4;
-                    }
-                    wave_lds_fence();   // the next pass writes the same region
+                for (int v = 0; v < 16; ++v) {
+                    const int q = qa + 8 * (v >> 2) + 4 * hh + (v & 3);
+                    const int p = q + off;
+                    bool ok = q < Sq && key_ok;
+                    if (causal) ok = ok && key <= p;
+                    if (window > 0) ok = ok && key > p - window;
+                    S[v] = ok ? S[v] : -INFINITY;
                 }
             }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 d4 = *reinterpret_cast<const float4*>(dlb + 8 * j + 4 * hh);
+                const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int v = 4 * j + i;
+                    S[v] = __builtin_amdgcn_exp2f(S[v]);
+                    P[v] = S[v] * (P[v] - dl[i]);
+                }
+            }
+            pb[0] = pack8(S, 0);
+            pb[1] = pack8(S, 1);
+            dsb[0] = pack8(P, 0);
+            dsb[1] = pack8(P, 1);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+
+        // dV^T += dO^T P, dK^T += Q^T dS; k step c covers the step's rows
+        // 16c .. 16c+15; operands one (c, d) pair ahead
+        auto backward_part = [&](const bf16x8* pb, const bf16x8* dsb, const unsigned char* qb, const unsigned char* ob)
+            __attribute__((always_inline)) {
+            bf16x8 to = tr_op<D>(ob, 0, 0, lane), tq = tr_op<D>(qb, 0, 0, lane);
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int x = 0; x < NP; ++x) {
+                const int c = x / DB, d = x % DB;
+                bf16x8 no = to, nq = tq;
+                if (x + 1 < NP) {
+                    no = tr_op<D>(ob, 16 * ((x + 1) / DB), (x + 1) % DB, lane);
+                    nq = tr_op<D>(qb, 16 * ((x + 1) / DB), (x + 1) % DB, lane);
+                }
+                dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to, pb[c], dv[d], 0, 0, 0);
+                dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq, dsb[c], dk[d], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                to = no;
+                tq = nq;
+            }
+            __builtin_amdgcn_s_setprio(0);
+        };
+
+        // step s, its tiles in the buffers of parity R (compile-time, so that
+        // every LDS address is a constant offset)
+        auto step = [&](int s, auto r2) __attribute__((always_inline)) {
+            constexpr int R = decltype(r2)::value;
+            if (s + 1 < s_end)
+                issue(s + 1, R ? q_lds0 : q_lds1, R ? o_lds0 : o_lds1, R ? l_lds0 : l_lds1, R ? d_lds0 : d_lds1);
+            bool edge;
+            if (visible_step(s, edge)) {
+                bf16x8 pb[2], dsb[2];
+                forward_part(R ? q_lds1 : q_lds0, R ? o_lds1 : o_lds0, R ? l_lds1 : l_lds0, R ? d_lds1 : d_lds0,
+                             tile_of(s) * kQB, edge, pb, dsb);
+                backward_part(pb, dsb, R ? q_lds1 : q_lds0, R ? o_lds1 : o_lds0);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        };
+
+        if (s_end > s_begin) {
+            // the workgroup's V rows stay in LDS for the whole kernel
+            dma_rows<D, kKvKeys, NW>(rsrc(V + kv_base, Sk * D * 2), k0, v_lds, wave, lane);
+            issue(s_begin, q_lds0, o_lds0, l_lds0, d_lds0);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            for (int s = s_begin; s < s_end; s += 2) {
+                step(s, std::integral_constant<int, 0>());
+                if (s + 1 < s_end) step(s + 1, std::integral_constant<int, 1>());
+            }
+        }
+
+        // accumulator value v of block db holds d = 32 db + 8(v/4) + 4hh + v%4
+        if (!wave_keys) return;
+        if (part != nullptr) {
+            const size_t plane = (size_t)nbg * Sk * D;
+            if constexpr (D == 128) {
+                // float partials, 64 columns (two d blocks, 256 bytes of a row)
+                // per pass through the wave's 8 KiB of V rows in LDS, read back
+                // as whole 256-byte row segments, four rows per store instruction
+                unsigned char* stage = v_lds + wave * (32 * D * 2);
+                const int cl = lane & 15;
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    float* base = part + (size_t)(m * nsplit + split) * plane + ((size_t)bg * Sk + kw0) * D;
+#pragma unroll
+                    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+                        for (int x = 0; x < 2; ++x)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const f32x16& acc = m == 0 ? dk[2 * pass + x] : dv[2 * pass + x];
+                                const float s = m == 0 ? scale : 1.f;
+                                const int chunk = (8 * x + 2 * r + hh) ^ (ln & 15);
+                                *reinterpret_cast<float4*>(stage + ln * 256 + chunk * 16) =
+                                    make_float4(acc[4 * r] * s, acc[4 * r + 1] * s, acc[4 * r + 2] * s,
+                                                acc[4 * r + 3] * s);
+                            }
+                        wave_lds_fence();
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const int row = 4 * i + (lane >> 4);
+                            const float4 v4 =
+                                *reinterpret_cast<const float4*>(stage + row * 256 + ((cl ^ (row & 15)) << 4));
+                            if (kw0 + row < Sk)
+                                *reinterpret_cast<float4*>(base + (size_t)row * D + 64 * pass + 4 * cl) = v4;
+                        }
+                        wave_lds_fence();   // the next pass writes the same region
+                    }
+                }
+                return;
+            }
+            if (!key_ok) return;
+            float* kp = part + (size_t)split * plane + ((size_t)bg * Sk + key) * D;
+            float* vp = part + (size_t)(nsplit + split) * plane + ((size_t)bg * Sk + key) * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int d = 32 * db + 8 * r + 4 * hh;
+                    *reinterpret_cast<float4*>(kp + d) =
+                        make_float4(dk[db][4 * r] * scale, dk[db][4 * r + 1] * scale, dk[db][4 * r + 2] * scale,
+                                    dk[db][4 * r + 3] * scale);
+                    *reinterpret_cast<float4*>(vp + d) =
+                        make_float4(dv[db][4 * r], dv[db][4 * r + 1], dv[db][4 * r + 2], dv[db][4 * r + 3]);
+                }
             return;
         }
-        if (!key_ok) return;
-        float* kp = part + (size_t)split * plane + ((size_t)bg * Sk + key) * D;
-        float* vp = part + (size_t)(nsplit + split) * plane + ((size_t)bg * Sk + key) * D;
+        // dK, then dV, through the wave's own V rows in LDS (no longer needed)
+        uint2 wk[DB][4], wv[DB][4];
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int d = 32 * db + 8 * r + 4 * hh;
-                *reinterpret_cast<float4*>(kp + d) = make_float4(dk[db][4 * r] * scale, dk[db][4 * r + 1] * scale,
-                                                                 dk[db][4 * r + 2] * scale, dk[db][4 * r + 3] * scale);
-                *reinterpret_cast<float4*>(vp + d) =
-                    make_float4(dv[db][4 * r], dv[db][4 * r + 1], dv[db][4 * r + 2], dv[db][4 * r + 3]);
+                wk[db][r] = pack4(dk[db][4 * r] * scale, dk[db][4 * r + 1] * scale, dk[db][4 * r + 2] * scale,
+                                  dk[db][4 * r + 3] * scale);
+                wv[db][r] = pack4(dv[db][4 * r], dv[db][4 * r + 1], dv[db][4 * r + 2], dv[db][4 * r + 3]);
             }
-        return;
+        unsigned char* stage = v_lds + wave * (32 * D * 2);
+        store_block<D>(stage, wk, dK + kv_base, kw0, Sk, lane);
+        store_block<D>(stage, wv, dV + kv_base, kw0, Sk, lane);
+    };
+    run_block(kt_first, true);
+    if (nblk == 2) {
+        __syncthreads();   // the V rows and the staging area are reused
+        run_block(pi, false);
     }
-    // dK, then dV, through the wave's own V rows in LDS (no longer needed)
-    uint2 wk[DB][4], wv[DB][4];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            wk[db][r] = pack4(dk[db][4 * r] * scale, dk[db][4 * r + 1] * scale, dk[db][4 * r + 2] * scale,
-                              dk[db][4 * r + 3] * scale);
-            wv[db][r] = pack4(dv[db][4 * r], dv[db][4 * r + 1], dv[db][4 * r + 2], dv[db][4 * r + 3]);
-        }
-    unsigned char* stage = v_lds + wave * (32 * D * 2);
-    store_block<D>(stage, wk, dK + kv_base, kw0, Sk, lane);
-    store_block<D>(stage, wv, dV + kv_base, kw0, Sk, lane);
 }
 
 // dK, dV of a split key block: the sum, in split order, of the runs' float32
@@ -768,16 +800,20 @@ hipError_t launch_d(const BackwardArgs& a, hipStream_t stream) {
     const int nbg = a.B * a.Hkv;
     const int nsplit = a.Sq > 0 ? a.kv_splits : 1;
     float* part = nsplit > 1 ? reinterpret_cast<float*>(ws + 2 * rbytes) : nullptr;
-    const long long grid = (long long)nbg * nkt * nsplit;
+    // causal, no window, one run per key block: key blocks in pairs (the
+    // light one first, top-down; the heavy one second, bottom-up), one round
+    // of equal work
+    const int paired = nsplit == 1 && a.causal && a.window == 0 && nkt >= 2 ? 1 : 0;
+    const long long grid = paired ? (long long)nbg * ((nkt + 1) / 2) : (long long)nbg * nkt * nsplit;
     if (!grid_fits(grid, 64 * kKvWaves)) return hipErrorInvalidValue;
     if (log_enabled())
-        log_dispatch("bwd_dkdv_kernel<%d>: grid %lld x %d threads, %d key blocks of %d per (batch, kv head), "
-                     "%d query splits%s", D, grid, 64 * kKvWaves, nkt, kKvKeys, nsplit,
+        log_dispatch("bwd_dkdv_kernel<%d>: grid %lld x %d threads, %d key blocks of %d per (batch, kv head)%s, "
+                     "%d query splits%s", D, grid, 64 * kKvWaves, nkt, kKvKeys, paired ? " in pairs" : "", nsplit,
                      nsplit > 1 ? " + bwd_kv_reduce_kernel" : "");
     hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)grid), dim3(64 * kKvWaves), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                        l2, delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.Hq, a.Hkv, a.Sq, a.Sk, a.scale, c2,
-                       a.causal, a.window, nbg, nsplit, part);
+                       a.causal, a.window, nbg, nsplit, part, nkt, paired);
     if (nsplit > 1) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
