@@ -146,3 +146,32 @@ def test_weight_ordered_rounds_head_groups():
         want = oracle.attention_bwd(f64(q[s]), f64(k[s]), f64(v[s]), f64(do[s]), scale, True, 0, row_chunk=1024)
         for name, g, w in zip(("dq", "dk", "dv"), (dq[s], dk[s], dv[s]), want):
             check_grad(f64(g), w, f"{name} b={b} h={h}")
+
+
+def test_paired_key_blocks_d64_odd_count():
+    # enough (batch, kv head, 128-key) blocks for one run each, so under a
+    # causal mask the dK/dV workgroups take key blocks in pairs: 65 blocks per
+    # (batch, kv head) (the middle one alone, the last one 33 keys), Sq < Sk
+    # (bottom-right), D = 64; outputs start as NaN so that a block no
+    # workgroup took shows up
+    B, Hq, Hkv, Sq, Sk, D = 2, 8, 4, 3000, 8225, 64
+    say(f"backward paired key blocks B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Sk={Sk} D={D}")
+    q, k, v = inputs.prefill_inputs(B, Hq, Hkv, Sq, Sk, D, "bf16", 64)
+    do = torch.randn((B, Hq, Sq, D), generator=torch.Generator().manual_seed(65)).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(D)
+    qd, kd, vd, dod = cuda(q, k, v, do)
+    o, lse = attn.fwd_lse(qd, kd, vd, scale=scale, causal=True)
+    outs = [torch.full_like(t, float("nan")) for t in (qd, kd, vd)]
+    attn.bwd(qd, kd, vd, o, dod, lse, scale=scale, causal=True, dq=outs[0], dk=outs[1], dv=outs[2])
+    torch.cuda.synchronize()
+    dq, dk, dv = (t.cpu() for t in outs)
+    assert all(torch.isfinite(t.float()).all() for t in (dq, dk, dv))
+    G = Hq // Hkv
+    for b, g in [(0, 0), (B - 1, Hkv - 1)]:
+        say(f"  oracle on batch {b}, kv head {g}")
+        hs = slice(g * G, (g + 1) * G)
+        want = oracle.attention_bwd(f64(q[b:b + 1, hs]), f64(k[b:b + 1, g:g + 1]), f64(v[b:b + 1, g:g + 1]),
+                                    f64(do[b:b + 1, hs]), scale, True, 0, row_chunk=1024)
+        check_grad(f64(dq[b:b + 1, hs]), want[0], f"dq b={b} g={g}")
+        check_grad(f64(dk[b:b + 1, g:g + 1]), want[1], f"dk b={b} g={g}")
+        check_grad(f64(dv[b:b + 1, g:g + 1]), want[2], f"dv b={b} g={g}")
